@@ -1,0 +1,218 @@
+"""CPU oracle for the packed Trellis-quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The product path (the HIP library and
+its Python binding) never imports this package, and this package imports
+nothing from the product path.
+
+The arithmetic lives in ``trellis_oracle.c`` (plain C, strict IEEE binary32
+with ``-ffp-contract=off``; float64 for the contraction). This module loads
+it with ctypes and wraps it for NumPy arrays. Source of the method: the web
+page "mlx-bun 0.2.0 -> 0.4.0" (npm diff, page 57), section
+``src/model/trellis-wide-prefill.ts``, Metal kernel body and host wrapper.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py``
+against facts that do not come from this code (exhaustive enumeration, exact
+rational arithmetic, closed forms, a second bit-level formulation, torch's
+bf16 cast, brute force). No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "trellis_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+             "-fno-builtin", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (strict IEEE flags). Returns the .so path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        c_int = ctypes.c_int
+        L.oracle_window.argtypes = [u32p, c_int, c_int]
+        L.oracle_window.restype = ctypes.c_uint32
+        L.oracle_code.argtypes = [ctypes.c_uint32]
+        L.oracle_code.restype = ctypes.c_int32
+        L.oracle_value.argtypes = [ctypes.c_int32]
+        L.oracle_value.restype = ctypes.c_float
+        L.oracle_reciprocal.argtypes = []
+        L.oracle_reciprocal.restype = ctypes.c_float
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_weight.argtypes = [ctypes.c_uint32, ctypes.c_uint16]
+        L.oracle_weight.restype = ctypes.c_uint16
+        L.oracle_decode_rows.argtypes = [u32p, u16p, c_int, c_int, c_int, c_int, u16p]
+        L.oracle_decode_rows.restype = None
+        L.oracle_prefill_rows.argtypes = [u16p, c_int, u32p, u16p, c_int, c_int, c_int,
+                                          c_int, f64p, f64p]
+        L.oracle_prefill_rows.restype = None
+        L.oracle_contract.argtypes = [u16p, c_int, u16p, c_int, c_int, f64p, f64p]
+        L.oracle_contract.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ---- scalar steps ---------------------------------------------------------
+
+def window(block: np.ndarray, bits: int, t: int) -> int:
+    """12-bit window of weight t in one block (array of 256*bits/32 uint32)."""
+    b = np.ascontiguousarray(block, dtype=np.uint32)
+    assert b.size == 256 * bits // 32
+    return int(lib().oracle_window(_ptr(b, ctypes.c_uint32), bits, t))
+
+
+def code(win: int) -> int:
+    return int(lib().oracle_code(win))
+
+
+def value(c: int) -> float:
+    """float32 value of an integer code (returned as a Python float)."""
+    return float(lib().oracle_value(c))
+
+
+def value_bits(c: int) -> int:
+    return int(np.array([value(c)], dtype=np.float32).view(np.uint32)[0])
+
+
+def reciprocal() -> float:
+    return float(lib().oracle_reciprocal())
+
+
+def f32_to_bf16(f: float) -> int:
+    return int(lib().oracle_f32_to_bf16(f))
+
+
+def bf16_to_f32(h: int) -> float:
+    return float(lib().oracle_bf16_to_f32(h))
+
+
+def weight(win: int, scale_bf16: int) -> int:
+    return int(lib().oracle_weight(win, scale_bf16))
+
+
+# ---- array entry points ---------------------------------------------------
+
+def _check(codes, scales, k, bits):
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    assert k % 256 == 0 and bits in (2, 3, 4)
+    assert codes.ndim == 2 and codes.shape[1] == k * bits // 32
+    assert scales.shape == (codes.shape[0],)
+    return codes, scales
+
+
+def decode_rows(codes, scales, k: int, bits: int, row0: int = 0, nrows: int | None = None):
+    """bf16 bit patterns of W[row0:row0+nrows, :K] (uint16 [nrows, K])."""
+    codes, scales = _check(codes, scales, k, bits)
+    n = codes.shape[0]
+    nrows = n - row0 if nrows is None else nrows
+    assert 0 <= row0 and row0 + nrows <= n
+    w = np.empty((nrows, k), dtype=np.uint16)
+    lib().oracle_decode_rows(_ptr(codes, ctypes.c_uint32), _ptr(scales, ctypes.c_uint16),
+                             k, bits, row0, nrows, _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def decode(codes, scales, k: int, bits: int):
+    return decode_rows(codes, scales, k, bits)
+
+
+def prefill_rows(x, codes, scales, k: int, bits: int, rows):
+    """float64 y[M, len(rows)] and a[M, len(rows)] = sum |w*x| for the listed rows.
+
+    rows is an iterable of output-row indices; consecutive runs are handed to
+    the C oracle in one call.
+    """
+    codes, scales = _check(codes, scales, k, bits)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m = x.shape[0]
+    assert x.shape == (m, k)
+    rows = np.asarray(list(rows), dtype=np.int64)
+    y = np.empty((m, rows.size), dtype=np.float64)
+    a = np.empty((m, rows.size), dtype=np.float64)
+    i = 0
+    while i < rows.size:
+        j = i + 1
+        while j < rows.size and rows[j] == rows[j - 1] + 1:
+            j += 1
+        cnt = j - i
+        yy = np.empty((m, cnt), dtype=np.float64)
+        aa = np.empty((m, cnt), dtype=np.float64)
+        lib().oracle_prefill_rows(_ptr(x, ctypes.c_uint16), m, _ptr(codes, ctypes.c_uint32),
+                                  _ptr(scales, ctypes.c_uint16), k, bits, int(rows[i]), cnt,
+                                  _ptr(yy, ctypes.c_double), _ptr(aa, ctypes.c_double))
+        y[:, i:j] = yy
+        a[:, i:j] = aa
+        i = j
+    return y, a
+
+
+def prefill(x, codes, scales, k: int, bits: int):
+    n = np.asarray(codes).shape[0]
+    return prefill_rows(x, codes, scales, k, bits, range(n))
+
+
+def contract(x, w):
+    """float64 y[M, N], a[M, N] from bf16 x[M, K] and an already decoded W[N, K]."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    m, k = x.shape
+    n = w.shape[0]
+    assert w.shape == (n, k)
+    y = np.empty((m, n), dtype=np.float64)
+    a = np.empty((m, n), dtype=np.float64)
+    lib().oracle_contract(_ptr(x, ctypes.c_uint16), m, _ptr(w, ctypes.c_uint16), k, n,
+                          _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
+    return y, a
+
+
+# ---- acceptance bound -----------------------------------------------------
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Unit in the last place of bf16 values v (float array of bf16 values).
+
+    2^(floor(log2|v|) - 7) for normal v; 2^-133 (the bf16 subnormal step)
+    for zero and subnormal v.
+    """
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    out = np.full(v.shape, 2.0 ** -133)
+    nz = v >= 2.0 ** -126
+    out[nz] = np.ldexp(1.0, (np.floor(np.log2(v[nz])) - 7).astype(np.int64))
+    return out
+
+
+def within_tolerance(out_bf16_bits: np.ndarray, y: np.ndarray, a: np.ndarray, rel: float = 1e-5):
+    """Boolean mask: |out - y| <= ulp_bf16(out) + rel * a (elementwise)."""
+    out = (np.asarray(out_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    out = out.astype(np.float64)
+    return np.abs(out - y) <= ulp_bf16(out) + rel * a
