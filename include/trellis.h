@@ -1,0 +1,111 @@
+/*
+ * trellis.h -- C ABI of the packed Trellis-quantized linear layer for
+ * narrow-batch prefill on AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes out[M, N] = x[M, K] . W^T in bf16, where W[N, K] is never
+ * stored: every weight is decoded on the fly from a packed code stream.
+ * Method: web page "mlx-bun 0.2.0 -> 0.4.0" (npm diff, page 57), section
+ * src/model/trellis-wide-prefill.ts -- the Metal kernel body (decode and
+ * narrow-M dot) and its host wrapper (shape and layout checks, eligibility
+ * predicate). The materialising decode corresponds to the "expand" mode named
+ * on the page "mlx-bun 0.4.0 -> 0.5.0" (npm diff, page 26), section
+ * src/model/trellis-linear.ts.
+ *
+ * Data formats (all buffers are caller-owned DEVICE memory):
+ *   bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   codes   uint32 [N, K*bits/32], row-major. Row n holds K/256 blocks of
+ *           256*bits/32 words (16, 24 or 32 words for bits = 2, 3, 4); block
+ *           b of row n starts at word n*(K*bits/32) + b*(256*bits/32).
+ *           Within a block the bits form one cyclic stream of 256*bits bits,
+ *           read LSB-first inside each word. Weight t of the block
+ *           (0 <= t < 256, column kk = 256*b + t) takes the 12 stream bits
+ *           starting at bit (255 - t)*bits, wrapping to the block's first
+ *           word past its end.
+ *   decode  window -> z = window*34038481 + 76625530 (mod 2^32);
+ *           code = (sum of the 4 bytes of z) - 510;
+ *           value = float32 code/147.800537109375 by the page's reciprocal
+ *           refinement; weight = bf16_RNE(float32(value * scale[n])).
+ *   scales  bf16 [N], one per output row.
+ *   x       bf16 [M, K], row-major, rows contiguous.
+ *   out     bf16 [M, N], row-major; out[m, n] = bf16_RNE(sum_kk W[n,kk]*x[m,kk])
+ *           accumulated in float32 (summation order is unspecified).
+ *
+ * Accepted domain (anything else is rejected before any GPU work):
+ *   T == 256, L == 12, bits in {2, 3, 4};
+ *   K % 256 == 0, 256 <= K <= TRELLIS_MAX_K;
+ *   N % 4 == 0, 4 <= N <= TRELLIS_MAX_N;
+ *   5 <= M <= 15 for trellis_prefill (the narrow-batch regime of the page's
+ *   eligibility predicate);
+ *   x, codes, out and w 16-byte aligned; scales 2-byte aligned; no pointer
+ *   NULL. The page's fixed K = 5120 is generalised to any multiple of 256.
+ *
+ * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without waiting. No call allocates,
+ * frees or synchronises, and none keeps any state between calls. Calls on
+ * different streams are independent. Errors are returned, never thrown;
+ * a validation error leaves every output untouched.
+ */
+#ifndef TRELLIS_H
+#define TRELLIS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRELLIS_T 256
+#define TRELLIS_L 12
+#define TRELLIS_MIN_M 5
+#define TRELLIS_MAX_M 15
+#define TRELLIS_MAX_K (1 << 18)
+#define TRELLIS_MAX_N (1 << 22)
+
+/* Geometry of one packed linear layer: n output rows (out features), k input
+ * columns (in features), block length t (must be 256), window length l (must
+ * be 12), bits per code (2, 3 or 4). */
+typedef struct trellis_geom {
+    int32_t n;
+    int32_t k;
+    int32_t t;
+    int32_t l;
+    int32_t bits;
+} trellis_geom;
+
+typedef enum trellis_status {
+    TRELLIS_OK = 0,
+    TRELLIS_E_GEOMETRY = -1, /* t, l, bits, n or k outside the accepted domain */
+    TRELLIS_E_M = -2,        /* m outside [5, 15] */
+    TRELLIS_E_NULL = -3,     /* a required pointer is NULL */
+    TRELLIS_E_ALIGN = -4,    /* a pointer is not aligned as documented */
+    TRELLIS_E_HIP = -5       /* the HIP runtime reported a launch error */
+} trellis_status;
+
+/* 1 if (g, m) is inside the accepted domain of trellis_prefill, else 0.
+ * Pure: no GPU access, no side effects. Mirrors the page's eligibility
+ * predicate (page 57, wideTrellisPrefillEligible) with K and N generalised. */
+int trellis_supported(trellis_geom g, int32_t m);
+
+/* Materialise W[N, K] as bf16 (w_bf16 is [N, K] row-major) from codes
+ * [N, K*bits/32] and scales [N]. The result is bit-exact: it has exactly one
+ * correct value per weight. Page 57, kernel body (decode steps); page 26,
+ * trellis-linear.ts (expand mode). */
+trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16,
+                              trellis_geom g, uint16_t *w_bf16, void *hip_stream);
+
+/* out[M, N] = x[M, K] . W^T with W decoded on the fly (page 57, kernel body
+ * and host wrapper). x is [m, K] bf16, out is [m, N] bf16, both row-major.
+ * Every output lies within 1 bf16 ulp of itself plus 1e-5 * sum|w*x| of the
+ * float64 sum of the same bf16 products. */
+trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m,
+                               const uint32_t *codes, const uint16_t *scales_bf16,
+                               trellis_geom g, uint16_t *out_bf16, void *hip_stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *trellis_status_string(trellis_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects every out-of-domain call before touching the GPU."""
+import os
+import re
+
+import pytest
+
+import trellis_coded_bit_prefill_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "trellis.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(trellis_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tp.LIB_PATH):
+        from trellis_coded_bit_prefill_amd import _build
+
+        _build.build()
+    return tp.load_library()
+
+
+def test_header_declares_the_bound_functions():
+    assert declared_functions() == sorted(tp.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in (tp.OK, tp.E_GEOMETRY, tp.E_M, tp.E_NULL, tp.E_ALIGN, tp.E_HIP):
+        assert tp.status_string(s)
+    assert tp.status_string(123) == "unknown status"
+
+
+GOOD = dict(n=17408, k=5120, bits=4)
+
+
+@pytest.mark.parametrize("n,k,bits,t,l,m,ok", [
+    (17408, 5120, 4, 256, 12, 5, True),
+    (17408, 5120, 3, 256, 12, 8, True),
+    (17408, 5120, 2, 256, 12, 15, True),
+    (5120, 17408, 4, 256, 12, 15, True),
+    (256, 512, 2, 256, 12, 5, True),
+    (4, 256, 2, 256, 12, 5, True),
+    (17408, 5120, 4, 256, 12, 4, False),   # m below the narrow-batch range
+    (17408, 5120, 4, 256, 12, 16, False),  # m above
+    (17408, 5120, 1, 256, 12, 5, False),   # bits
+    (17408, 5120, 5, 256, 12, 5, False),
+    (17408, 5120, 8, 256, 12, 5, False),
+    (17408, 5120, 4, 128, 12, 5, False),   # block length
+    (17408, 5120, 4, 256, 16, 5, False),   # window length
+    (17408, 5000, 4, 256, 12, 5, False),   # K not a multiple of 256
+    (17408, 0, 4, 256, 12, 5, False),
+    (17406, 5120, 4, 256, 12, 5, False),   # N not a multiple of 4
+    (0, 5120, 4, 256, 12, 5, False),
+    (-4, 5120, 4, 256, 12, 5, False),
+    (17408, (1 << 18) + 256, 4, 256, 12, 5, False),
+    ((1 << 22) + 4, 256, 4, 256, 12, 5, False),
+])
+def test_supported_truth_table(lib, n, k, bits, t, l, m, ok):
+    assert tp.supported(tp.geom(n, k, bits, t, l), m) is ok
+
+
+FAKE = 1 << 20  # a 16-byte aligned, never dereferenced address
+
+
+def call_prefill(x=FAKE, m=5, codes=FAKE, scales=FAKE, g=None, out=FAKE):
+    g = g or tp.geom(**GOOD)
+    return tp.load_library().trellis_prefill(x, m, codes, scales, g, out, None)
+
+
+def call_decode(codes=FAKE, scales=FAKE, g=None, w=FAKE):
+    g = g or tp.geom(**GOOD)
+    return tp.load_library().trellis_decode(codes, scales, g, w, None)
+
+
+def test_prefill_rejects_before_launch(lib):
+    assert call_prefill(g=tp.geom(17408, 5000, 4)) == tp.E_GEOMETRY
+    assert call_prefill(g=tp.geom(17408, 5120, 5)) == tp.E_GEOMETRY
+    assert call_prefill(m=4) == tp.E_M
+    assert call_prefill(m=16) == tp.E_M
+    assert call_prefill(x=None) == tp.E_NULL
+    assert call_prefill(codes=None) == tp.E_NULL
+    assert call_prefill(scales=None) == tp.E_NULL
+    assert call_prefill(out=None) == tp.E_NULL
+    assert call_prefill(x=FAKE + 2) == tp.E_ALIGN
+    assert call_prefill(codes=FAKE + 4) == tp.E_ALIGN
+    assert call_prefill(out=FAKE + 8) == tp.E_ALIGN
+    assert call_prefill(scales=FAKE + 1) == tp.E_ALIGN
+    # geometry is checked first, then m, then pointers
+    assert call_prefill(g=tp.geom(17408, 5000, 4), m=4, x=None) == tp.E_GEOMETRY
+    assert call_prefill(m=4, x=None) == tp.E_M
+
+
+def test_decode_rejects_before_launch(lib):
+    assert call_decode(g=tp.geom(17408, 5120, 4, 128)) == tp.E_GEOMETRY
+    assert call_decode(g=tp.geom(17406, 5120, 4)) == tp.E_GEOMETRY
+    assert call_decode(codes=None) == tp.E_NULL
+    assert call_decode(scales=None) == tp.E_NULL
+    assert call_decode(w=None) == tp.E_NULL
+    assert call_decode(codes=FAKE + 4) == tp.E_ALIGN
+    assert call_decode(w=FAKE + 2) == tp.E_ALIGN
+    assert call_decode(scales=FAKE + 1) == tp.E_ALIGN
+
+
+def test_python_binding_raises_value_error_on_validation(lib):
+    with pytest.raises(ValueError):
+        tp.prefill_raw(FAKE, 4, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)
+    with pytest.raises(ValueError):
+        tp.decode_raw(FAKE, FAKE, tp.geom(17408, 5120, 7), FAKE, 0)

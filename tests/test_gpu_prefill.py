@@ -1,0 +1,119 @@
+"""trellis_prefill on the GPU against the float64 CPU oracle.
+
+Acceptance: |out - y| <= ulp_bf16(out) + 1e-5 * sum|w*x| elementwise, y the
+float64 sum of the same bf16 products. One-hot activations make the sum a
+single exact term, so those outputs must equal the decoded weights bit for
+bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import trellis_coded_bit_prefill_amd as tp
+from workloads import SHAPES, generate, generate_shape
+from tests.helpers import assert_prefill_close, from_dev_bf16, to_dev_bf16, to_dev_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tp.load_library()
+
+
+def gpu_prefill(x, codes, scales, bits):
+    import torch
+
+    out = tp.prefill(to_dev_bf16(x), to_dev_codes(codes), to_dev_bf16(scales), bits)
+    torch.cuda.synchronize()
+    return from_dev_bf16(out)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("m", [5, 8, 15])
+@pytest.mark.parametrize("n,k", [(4, 256), (68, 768), (324, 1792)])
+def test_prefill_small_shapes(bits, m, n, k):
+    print(f"prefill small m={m} n={n} k={k} bits={bits}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=2000 + 7 * m + n + k + bits)
+    out = gpu_prefill(x, codes, scales, bits)
+    y, a = oracle.prefill(x, codes, scales, k, bits)
+    assert_prefill_close(out, y, a, f"m={m} n={n} k={k} bits={bits}")
+
+
+@pytest.mark.parametrize("m", list(range(5, 16)))
+def test_prefill_every_m(m):
+    print(f"prefill every m={m}", flush=True)
+    x, codes, scales = generate(m, 1024, 132, 3, seed=3000 + m)
+    out = gpu_prefill(x, codes, scales, 3)
+    y, a = oracle.prefill(x, codes, scales, 1024, 3)
+    assert_prefill_close(out, y, a, f"m={m}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "wide_m5_k4", "wide_m8_k3", "wide_m15_k2", "down_m15_k4"])
+def test_prefill_full_shapes(name):
+    s = SHAPES[name]
+    print(f"prefill full shape {name}", flush=True)
+    x, codes, scales = generate_shape(s)
+    out = gpu_prefill(x, codes, scales, s.bits)
+    assert out.shape == (s.m, s.n)
+    if s.n <= 4096:
+        rows = np.arange(s.n)
+    else:
+        rng = np.random.default_rng(11)
+        rows = np.unique(np.concatenate([np.arange(64), np.arange(s.n - 64, s.n),
+                                         rng.integers(0, s.n, 384)]))
+    y, a = oracle.prefill_rows(x, codes, scales, s.k, s.bits, rows)
+    assert_prefill_close(out[:, rows], y, a, name)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_prefill_one_hot_rows_equal_decoded_weights(bits):
+    print(f"prefill one-hot bits={bits}", flush=True)
+    k, n = 1024, 196
+    _, codes, scales = generate(5, k, n, bits, seed=4000 + bits)
+    cols = [0, 1, 7, 8, 255, 256, 257, 511, 512, 640, 767, 768, 1000, 1023, 100]
+    x = np.zeros((len(cols), k), dtype=np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3F80  # 1.0
+    out = gpu_prefill(x, codes, scales, bits)
+    w = oracle.decode(codes, scales, k, bits)
+    assert np.array_equal(out, w[:, cols].T)
+
+
+def test_prefill_zero_codes_closed_form():
+    # All-zero codes decode every weight to bf16(v0 * s_n), v0 = value(window 0).
+    k, n, m = 768, 36, 9
+    x, _, scales = generate(m, k, n, 4, seed=4100)
+    codes = np.zeros((n, k * 4 // 32), dtype=np.uint32)
+    out = gpu_prefill(x, codes, scales, 4)
+    y, a = oracle.prefill(x, codes, scales, k, 4)
+    assert_prefill_close(out, y, a, "zero codes")
+
+
+def test_prefill_is_deterministic():
+    s = SHAPES["wide_m8_k3"]
+    x, codes, scales = generate_shape(s)
+    import torch
+
+    xd, cd, sd = to_dev_bf16(x), to_dev_codes(codes), to_dev_bf16(scales)
+    o1 = tp.prefill(xd, cd, sd, s.bits)
+    o2 = tp.prefill(xd, cd, sd, s.bits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_prefill_rejects_bad_m_on_device():
+    import torch
+
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros((4, 32), dtype=torch.int32, device="cuda")
+    scales = torch.zeros((4,), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        tp.prefill(x, codes, scales, 4)
+    x16 = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        tp.prefill(x16, codes, scales, 4)

@@ -1,0 +1,199 @@
+"""Packed Trellis-quantized linear layer for narrow-batch prefill on MI355X.
+
+Thin ctypes binding over the C ABI in ``include/trellis.h`` (library
+``libtrellis.so``, hand-written HIP for gfx950). The functions here only
+marshal torch tensors into device pointers, sizes and the current HIP
+stream; every step of the layer runs in the library's kernels. There is no
+CPU fallback: if the library is missing or fails to load, importing the
+entry points raises.
+
+Method: web page "mlx-bun 0.2.0 -> 0.4.0" (npm diff, page 57), section
+src/model/trellis-wide-prefill.ts (kernel body and host wrapper).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtrellis.so")
+
+T_BLOCK = 256
+L_WINDOW = 12
+MIN_M = 5
+MAX_M = 15
+
+OK = 0
+E_GEOMETRY = -1
+E_M = -2
+E_NULL = -3
+E_ALIGN = -4
+E_HIP = -5
+
+# Every symbol declared in include/trellis.h.
+EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_status_string")
+
+
+class Geom(ctypes.Structure):
+    """trellis_geom: n output rows, k input columns, block t, window l, bits."""
+
+    _fields_ = [("n", ctypes.c_int32), ("k", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("l", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+def geom(n: int, k: int, bits: int, t: int = T_BLOCK, l: int = L_WINDOW) -> Geom:
+    return Geom(n, k, t, l, bits)
+
+
+class TrellisError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"trellis status {status}: {msg}")
+        self.status = status
+
+
+class TrellisValueError(TrellisError, ValueError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtrellis.so (raises OSError if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is not built; run trellis_coded_bit_prefill_amd/_build.py")
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.trellis_supported.argtypes = [Geom, ctypes.c_int32]
+    L.trellis_supported.restype = ctypes.c_int
+    L.trellis_status_string.argtypes = [ctypes.c_int]
+    L.trellis_status_string.restype = ctypes.c_char_p
+    L.trellis_decode.argtypes = [vp, vp, Geom, vp, vp]
+    L.trellis_decode.restype = ctypes.c_int
+    L.trellis_prefill.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
+    L.trellis_prefill.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().trellis_status_string(status).decode()
+
+
+def supported(g: Geom, m: int) -> bool:
+    return bool(load_library().trellis_supported(g, m))
+
+
+def _raise(status: int):
+    if status == OK:
+        return
+    msg = status_string(status)
+    if status == E_HIP:
+        raise TrellisError(status, msg)
+    raise TrellisValueError(status, msg)
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(name, t, dtypes, ndim, device=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} dtype {t.dtype} not in {dtypes}")
+    if t.ndim != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dtypes():
+    import torch
+
+    return ((torch.bfloat16, torch.int16, torch.uint16),  # bf16 bit patterns
+            (torch.int32, torch.uint32))                  # code words
+
+
+def decode_raw(codes_ptr: int, scales_ptr: int, g: Geom, w_ptr: int, stream: int) -> None:
+    """Direct C-ABI call with raw device addresses."""
+    _raise(load_library().trellis_decode(codes_ptr, scales_ptr, g, w_ptr, stream))
+
+
+def prefill_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out_ptr: int,
+                stream: int) -> None:
+    """Direct C-ABI call with raw device addresses."""
+    _raise(load_library().trellis_prefill(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
+
+
+@dataclass
+class Layer:
+    """A packed Trellis linear layer: codes [N, K*bits/32] and scales [N]."""
+
+    codes: "object"
+    scales: "object"
+    n: int
+    k: int
+    bits: int
+
+    @property
+    def geom(self) -> Geom:
+        return geom(self.n, self.k, self.bits)
+
+
+def decode(codes, scales, k: int, bits: int, out=None):
+    """Materialise W[N, K] (bf16) from packed codes on the current stream."""
+    import torch
+
+    bf, cw = _dtypes()
+    _check_tensor("codes", codes, cw, 2)
+    _check_tensor("scales", scales, bf, 1, codes.device)
+    n = codes.shape[0]
+    if codes.shape[1] * 32 != k * bits:
+        raise ValueError(f"codes has {codes.shape[1]} words per row, expected K*bits/32 = {k * bits // 32}")
+    if scales.shape[0] != n:
+        raise ValueError("scales must have one entry per row")
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=codes.device)
+    _check_tensor("out", out, bf, 2, codes.device)
+    if tuple(out.shape) != (n, k):
+        raise ValueError("out must be [N, K]")
+    decode_raw(codes.data_ptr(), scales.data_ptr(), geom(n, k, bits), out.data_ptr(),
+               _stream_handle(codes.device))
+    return out
+
+
+def prefill(x, codes, scales, bits: int, out=None):
+    """out[M, N] = x[M, K] . W^T (bf16), W decoded on the fly, current stream."""
+    import torch
+
+    bf, cw = _dtypes()
+    _check_tensor("x", x, bf, 2)
+    _check_tensor("codes", codes, cw, 2, x.device)
+    _check_tensor("scales", scales, bf, 1, x.device)
+    m, k = x.shape
+    n = codes.shape[0]
+    if codes.shape[1] * 32 != k * bits:
+        raise ValueError(f"codes has {codes.shape[1]} words per row, expected K*bits/32 = {k * bits // 32}")
+    if scales.shape[0] != n:
+        raise ValueError("scales must have one entry per row")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check_tensor("out", out, bf, 2, x.device)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M, N]")
+    prefill_raw(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), geom(n, k, bits),
+                out.data_ptr(), _stream_handle(x.device))
+    return out

@@ -1,0 +1,104 @@
+// Device-side decode arithmetic of the packed Trellis code stream (gfx950).
+//
+// Method: web page "mlx-bun 0.2.0 -> 0.4.0" (npm diff, page 57), section
+// src/model/trellis-wide-prefill.ts, kernel body: 12-bit cyclic window at
+// stream bit (255 - t)*k of the weight's 256-weight block (LSB-first words,
+// the block's first word follows its last), 1MAD hash, byte sum minus 510,
+// float32 reciprocal refinement by C = 147.800537109375, per-row scale, bf16.
+//
+// Three equivalent ways to reach the bf16 weight live here:
+//   * trellis_value(): the refinement exactly as the page orders it; used to
+//     build the per-workgroup 4096-entry window -> value table and by the
+//     materialising decode kernel;
+//   * the table path: value = table[window], weight = bf16(value * scale);
+//   * the ALU path: weight = bf16(float(code) * q), q = float32(scale * r),
+//     r = float32(1/C). For every code in [-510, 510] and every bf16 scale
+//     mantissa this gives the same bf16 as the page's chain (checked
+//     exhaustively on the CPU and, for the GPU, by the decode tests); scaling
+//     by a power of two commutes with every rounding involved as long as all
+//     intermediates stay normal, which holds for 2^-110 <= |scale| <= 2^110.
+//     Rows whose scale lies outside that range (or is not finite) use the
+//     table path only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trellis {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kC = 147.800537109375f;
+constexpr float kR = 1.0f / kC;  // IEEE division folded at compile time
+
+// 1MAD hash of a 12-bit window: win * 34038481 + 76625530 (mod 2^32).
+// 34038481 = 2*2^24 + 0x0762D1, so for win < 2^24 the product is one
+// 24-bit multiply-add plus (win << 25): two full-rate VALU ops instead of a
+// quarter-rate 32-bit multiply.
+__device__ __forceinline__ uint32_t hash_1mad(uint32_t win) {
+  uint32_t t, z;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(t) : "v"(win), "s"(0x0762D1u), "v"(76625530u));
+  asm("v_lshl_add_u32 %0, %1, 25, %2" : "=v"(z) : "v"(win), "v"(t));
+  return z;
+}
+
+// Byte sum of the hash minus 510. v_sad_u8(z, 0, acc) adds the four bytes of
+// z to acc; acc = -510 (mod 2^32) yields the signed code.
+__device__ __forceinline__ int code_of(uint32_t win) {
+  return (int)__builtin_amdgcn_sad_u8(hash_1mad(win), 0u, 0xFFFFFE02u);
+}
+
+// The page's normalisation: a = c*r, residual = fma(-a, C, c), a + residual*r.
+__device__ __forceinline__ float trellis_value(int code) {
+  const float c = (float)code;
+  const float a = c * kR;
+  const float residual = __builtin_fmaf(-a, kC, c);
+  return __builtin_fmaf(residual, kR, a);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// Scales for which the ALU path is exact (see the file comment).
+__device__ __forceinline__ bool alu_scale_ok(float s) {
+  const float a = __builtin_fabsf(s);
+  return a == 0.0f || (a >= 0x1p-110f && a <= 0x1p110f);
+}
+
+// ---- window extraction from a lane's registers ----------------------------
+// D[] holds consecutive code words of one block (LSB-first); O is the bit
+// offset of the window's lowest bit inside D (compile-time).
+
+// The 12-bit window itself.
+template <int O, int N>
+__device__ __forceinline__ uint32_t win12(const uint32_t (&D)[N]) {
+  constexpr int w = O >> 5, b = O & 31;
+  static_assert(w < N, "window start outside the lane's words");
+  if constexpr (b + 12 <= 32) {
+    return __builtin_amdgcn_ubfe(D[w], b, 12);
+  } else {
+    static_assert(w + 1 < N, "straddling window needs the next word");
+    return __builtin_amdgcn_alignbit(D[w + 1], D[w], b) & 0xFFFu;
+  }
+}
+
+// The window times 4: the byte address of its entry in a float table.
+template <int O, int N>
+__device__ __forceinline__ uint32_t win_x4(const uint32_t (&D)[N]) {
+  constexpr int w = O >> 5, b = O & 31;
+  static_assert(w < N, "window start outside the lane's words");
+  if constexpr (b >= 2) {
+    if constexpr (b + 12 <= 32) {
+      return (D[w] >> (b - 2)) & 0x3FFCu;
+    } else {
+      static_assert(w + 1 < N, "straddling window needs the next word");
+      return __builtin_amdgcn_alignbit(D[w + 1], D[w], b - 2) & 0x3FFCu;
+    }
+  } else {
+    return (D[w] << (2 - b)) & 0x3FFCu;
+  }
+}
+
+}  // namespace trellis

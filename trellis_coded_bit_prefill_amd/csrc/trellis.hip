@@ -1,0 +1,510 @@
+// Packed Trellis-quantized linear layer for narrow-batch prefill, gfx950.
+//
+// Method: web page "mlx-bun 0.2.0 -> 0.4.0" (npm diff, page 57), section
+// src/model/trellis-wide-prefill.ts -- Metal kernel body (window extraction,
+// 1MAD hash, byte sum, reciprocal-refinement normalisation, per-row scale,
+// bf16 rounding, narrow-M dot product) and host wrapper (shape checks). The
+// materialising decode is the "expand" mode of page "mlx-bun 0.4.0 -> 0.5.0"
+// (npm diff, page 26), section src/model/trellis-linear.ts.
+//
+// CDNA4 design (not a translation of the Metal kernel):
+//   * one persistent workgroup per CU; the work is a list of units (16-row
+//     tile x one 256-weight block) split into equal contiguous ranges per
+//     wave (stream-K), so every SIMD gets the same decode work;
+//   * x is staged once per workgroup in LDS (a K panel of it when all of x
+//     does not fit) with an all-zero row that pads M up to 16;
+//   * each lane loads the code words of 64 consecutive weights of one row
+//     (coalesced dwordx4/x2 loads) and decodes them in registers, part of
+//     them through a 4096-entry window -> value table in LDS and part of them
+//     with ALU arithmetic (the two resources run in parallel);
+//   * bf16 MFMA 16x16x32: A = x (rows padded to 16), B = W^T (16 rows);
+//   * tiles shared by several waves are summed in a fixed order through a
+//     small workspace, the last contributor (per-tile counter) writing bf16.
+//
+// Build flags that matter for exactness: -ffp-contract=off.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "decode.hpp"
+#include "trellis.h"
+
+namespace trellis {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 8;                  // waves per prefill workgroup
+constexpr int kWgThreads = kWave * kWaves;
+constexpr int kTableBytes = 4096 * 4;      // window -> float value
+constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
+constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
+
+// ---------------------------------------------------------------------------
+// trellis_decode: W[N, K] bf16. One thread per 8 consecutive weights of one
+// row, one 16-byte store each. Weights t = 8q .. 8q+7 of a block start at
+// stream bits (255 - t)*BITS; weight 8q+7 is the lowest, at (248 - 8q)*BITS,
+// and the eight windows span 7*BITS + 12 <= 40 bits, inside the 64-bit pair
+// of the start word and the next word of the same block (cyclic).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict__ codes,
+                                                     const uint16_t *__restrict__ scales, int n, int k,
+                                                     uint16_t *__restrict__ w) {
+  constexpr int wpb = 8 * BITS;
+  const int groups_per_row = k >> 3;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)n * groups_per_row) return;
+  const int row = (int)(gid / groups_per_row);
+  const int c8 = (int)(gid - (int64_t)row * groups_per_row);
+  const int q = c8 & 31;
+  const uint32_t *bw = codes + (int64_t)row * (k >> 8) * wpb + (int64_t)(c8 >> 5) * wpb;
+  const int start = (248 - 8 * q) * BITS;
+  const int d = start >> 5, off = start & 31;
+  const uint64_t f = ((uint64_t)bw[d + 1 == wpb ? 0 : d + 1] << 32) | (uint64_t)bw[d];
+  const float scale = bf16_bits_to_f32(scales[row]);
+  bf16x8 v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const uint32_t win = (uint32_t)(f >> (off + (7 - s) * BITS)) & 0xFFFu;
+    v[s] = (__bf16)(trellis_value(code_of(win)) * scale);
+  }
+  *reinterpret_cast<bf16x8 *>(w + (int64_t)row * k + (int64_t)c8 * 8) = v;
+}
+
+// ---------------------------------------------------------------------------
+// trellis_prefill
+// ---------------------------------------------------------------------------
+
+// Work partition, computed on the host and re-derived by every wave.
+struct Plan {
+  int32_t m, n, k;
+  int32_t tiles;     // ceil(N / 16)
+  int32_t panels;    // K panels (x panel staged per workgroup)
+  int32_t kp;        // 256-weight blocks per panel
+  int32_t groups;    // workgroups per panel
+  int32_t maxc;      // contributor slots per (tile, panel) in the workspace
+  int32_t x_stride;  // bytes per staged x row
+  int32_t lds_bytes;
+  int64_t units;     // tiles * kp (per panel)
+  int64_t nw;        // active waves per panel: min(groups * waves, units)
+};
+
+__device__ __forceinline__ int64_t owner_of(int64_t u, int64_t nw, int64_t units) {
+  // The wave whose range [floor(w*U/V), floor((w+1)*U/V)) holds unit u.
+  return ((u + 1) * nw - 1) / units;
+}
+
+// Lane (j, g) of a wave: j = row of the 16-row tile (B column) and x row (A
+// row); g = k-group. For each block the lane owns stream bits
+// [64*BITS*g, 64*BITS*(g+1)) -- words [2*BITS*g, 2*BITS*(g+1)) -- plus the
+// next word of the block (cyclic) for the windows that run past its range.
+// Those are the windows of weights t = 192 - 64g + idx, idx = 0..63: weight
+// idx sits at local bit (63 - idx)*BITS. MFMA group u (0..7) takes
+// idx = 8u .. 8u+7 for both A and B, so x and W meet at the same k.
+template <int BITS>
+struct LaneWords {
+  uint32_t d[2 * BITS + 1];
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_words(const uint32_t *__restrict__ blk, int g, LaneWords<BITS> &L) {
+  constexpr int wpb = 8 * BITS;
+  const uint32_t *p = blk + 2 * BITS * g;
+  if constexpr (BITS == 4) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    const uint4 b = *reinterpret_cast<const uint4 *>(p + 4);
+    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = a.z; L.d[3] = a.w;
+    L.d[4] = b.x; L.d[5] = b.y; L.d[6] = b.z; L.d[7] = b.w;
+  } else if constexpr (BITS == 3) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    const uint2 b = *reinterpret_cast<const uint2 *>(p + 2);
+    const uint2 c = *reinterpret_cast<const uint2 *>(p + 4);
+    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = b.x; L.d[3] = b.y; L.d[4] = c.x; L.d[5] = c.y;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = a.z; L.d[3] = a.w;
+  }
+  L.d[2 * BITS] = blk[(2 * BITS * (g + 1)) % wpb];
+}
+
+__device__ __forceinline__ float lds_table(const unsigned char *table, uint32_t byte_addr) {
+  return *reinterpret_cast<const float *>(table + byte_addr);
+}
+
+template <int BITS, int U, int... S>
+__device__ __forceinline__ bf16x8 group_table(const LaneWords<BITS> &L, const unsigned char *table, float s,
+                                              std::integer_sequence<int, S...>) {
+  const float f[8] = {(lds_table(table, win_x4<(63 - 8 * U - S) * BITS>(L.d)) * s)...};
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
+  return w;
+}
+
+template <int BITS, int U, int... S>
+__device__ __forceinline__ bf16x8 group_alu(const LaneWords<BITS> &L, float q, std::integer_sequence<int, S...>) {
+  const float f[8] = {((float)code_of(win12<(63 - 8 * U - S) * BITS>(L.d)) * q)...};
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
+  return w;
+}
+
+// One unit: 8 MFMA groups over the lane's 64 weights of one block.
+template <int BITS, int MASK, int U>
+__device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsigned char *table,
+                                           const unsigned char *xa, float s, float q, f32x4 &acc) {
+  bf16x8 w;
+  if constexpr ((MASK >> U) & 1)
+    w = group_table<BITS, U>(L, table, s, std::make_integer_sequence<int, 8>{});
+  else
+    w = group_alu<BITS, U>(L, q, std::make_integer_sequence<int, 8>{});
+  const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+}
+
+template <int BITS, int MASK, int... U>
+__device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned char *table, const unsigned char *xa,
+                                     float s, float q, f32x4 &acc, std::integer_sequence<int, U...>) {
+  (unit_group<BITS, MASK, U>(L, table, xa, s, q, acc), ...);
+}
+
+__device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
+  if (row >= n) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * g + e;
+    if (i < m) out[(int64_t)i * n + row] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+  }
+}
+
+// Finish a tile: sole contributor writes bf16 directly; otherwise publish the
+// partial and let the last arriving contributor add all partials in slot
+// order (fixed, so the result does not depend on arrival order).
+//
+// Cross-CU visibility without cache-wide maintenance: partials are written
+// and read with agent-scope relaxed atomics (coherent at the device level,
+// across the per-XCD L2s), and every lane's stores are complete
+// (s_waitcnt vmcnt(0)) before lane 0 bumps the tile counter. The last
+// arriver's loads are issued only after its counter update returned, so
+// they observe every published partial. A full __threadfence() would write
+// back and invalidate the whole L2 at each flush instead.
+__device__ __forceinline__ void flush_tile(const Plan &pl, int tile, int panel, int64_t wave_id, int64_t nw,
+                                        f32x4 acc, float *__restrict__ ws, uint32_t *__restrict__ counters,
+                                        uint16_t *__restrict__ out, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int row = tile * 16 + j;
+  const int64_t first = (int64_t)tile * pl.kp;
+  const int64_t o0 = owner_of(first, nw, pl.units);
+  const int64_t o1 = owner_of(first + pl.kp - 1, nw, pl.units);
+  const int contrib = (int)(o1 - o0 + 1);
+  const int total = contrib * pl.panels;
+  if (total == 1) {
+    store_tile(out, acc, pl.m, pl.n, row, g);
+    return;
+  }
+  float *slot = ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + (wave_id - o0)) * 256 + 4 * lane;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) __hip_atomic_store(slot + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != (uint32_t)(total - 1)) return;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int pp = 0; pp < pl.panels; ++pp)
+    for (int cc = 0; cc < contrib; ++cc) {
+      float *src = ws + (((int64_t)tile * pl.panels + pp) * pl.maxc + cc) * 256 + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  store_tile(out, sum, pl.m, pl.n, row, g);
+  if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BITS, int MASK>
+__global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__restrict__ x,
+                                                             const uint32_t *__restrict__ codes,
+                                                             const uint16_t *__restrict__ scales,
+                                                             uint16_t *__restrict__ out, float *__restrict__ ws,
+                                                             uint32_t *__restrict__ counters, Plan pl) {
+  // The table is static LDS (address known at compile time, so table reads
+  // carry their base in the instruction offset); x follows it dynamically.
+  __shared__ __attribute__((aligned(16))) float s_table[4096];
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
+  unsigned char *const xl = lds;
+  constexpr int wpb = 8 * BITS;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int panel = blockIdx.x % pl.panels;
+  const int group = blockIdx.x / pl.panels;
+  const int panel_k = pl.kp * 256;
+  const int64_t kbase = (int64_t)panel * panel_k;
+
+  // Stage x[:, panel] (M rows) and an all-zero row M.
+  const int vecs = panel_k / 8;
+  for (int v = tid; v < (pl.m + 1) * vecs; v += kWgThreads) {
+    const int i = v / vecs, c = v - i * vecs;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (i < pl.m) val = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
+    *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = val;
+  }
+  // Window -> value table, by the page's arithmetic.
+  for (int e = tid; e < 4096; e += kWgThreads) s_table[e] = trellis_value(code_of((uint32_t)e));
+  __syncthreads();
+
+  const int j = lane & 15, g = lane >> 4;
+  // Every active wave gets a non-empty range because nw <= units; waves
+  // beyond nw (tiny problems only) have nothing to do.
+  const int64_t nw = pl.nw;
+  const int64_t wave_id = (int64_t)group * kWaves + wave;
+  const int64_t u0 = wave_id < nw ? wave_id * pl.units / nw : 0;
+  const int64_t u1 = wave_id < nw ? (wave_id + 1) * pl.units / nw : 0;
+  const int64_t row_words = (int64_t)(pl.k >> 8) * wpb;
+  const unsigned char *xa = xl + (j < pl.m ? j : pl.m) * pl.x_stride + (192 - 64 * g) * 2;
+
+  int cur = -1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float s = 0.f, q = 0.f;
+  bool table_only = false;
+  const uint32_t *rowp = codes;
+  bool row_ok = false;
+  // (tile, b) of unit u0, then stepped without dividing.
+  int tile = (int)(u0 / pl.kp);
+  int b = (int)(u0 - (int64_t)tile * pl.kp);
+  for (int64_t u = u0; u < u1; ++u, ++b) {
+    if (b == pl.kp) {
+      b = 0;
+      ++tile;
+    }
+    if (tile != cur) {
+      if (cur >= 0) flush_tile(pl, cur, panel, wave_id, nw, acc, ws, counters, out, lane);
+      cur = tile;
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = tile * 16 + j;
+      row_ok = row < pl.n;
+      s = row_ok ? bf16_bits_to_f32(scales[row]) : 0.f;
+      q = s * kR;
+      table_only = !__all(alu_scale_ok(s));
+      rowp = codes + (int64_t)(row_ok ? row : 0) * row_words + (int64_t)panel * pl.kp * wpb;
+    }
+    LaneWords<BITS> L;
+    if (row_ok) {
+      load_words<BITS>(rowp + (int64_t)b * wpb, g, L);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * BITS + 1; ++i) L.d[i] = 0u;
+    }
+    const unsigned char *xb = xa + b * 512;
+    if (table_only)
+      unit<BITS, 0xFF>(L, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+    else
+      unit<BITS, MASK>(L, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+  }
+  if (cur >= 0) flush_tile(pl, cur, panel, wave_id, nw, acc, ws, counters, out, lane);
+}
+
+// Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
+// use ALU arithmetic.
+template <int BITS> struct Mix;
+template <> struct Mix<2> { static constexpr int kMask = 0b01011011; };
+template <> struct Mix<3> { static constexpr int kMask = 0b01011011; };
+template <> struct Mix<4> { static constexpr int kMask = 0b01011011; };
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+bool geometry_ok(const trellis_geom &g) {
+  if (g.t != TRELLIS_T || g.l != TRELLIS_L) return false;
+  if (g.bits != 2 && g.bits != 3 && g.bits != 4) return false;
+  if (g.k < TRELLIS_T || g.k > TRELLIS_MAX_K || g.k % TRELLIS_T != 0) return false;
+  if (g.n < 4 || g.n > TRELLIS_MAX_N || g.n % 4 != 0) return false;
+  return true;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The launch macro reports configuration errors through the thread's last
+// error; it is cleared before each launch so a stale error from an unrelated
+// earlier call is not reported as ours.
+void clear_last_error() { (void)hipGetLastError(); }
+trellis_status launch_status() { return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_E_HIP; }
+
+Plan make_plan(int m, int n, int k, int cus) {
+  Plan pl{};
+  pl.m = m;
+  pl.n = n;
+  pl.k = k;
+  pl.tiles = (n + 15) / 16;
+  const int kb = k / 256;
+  int panels = kb;
+  for (int p = 1; p <= kb; ++p) {
+    if (kb % p) continue;
+    const int stride = (kb / p) * 512 + 16;
+    if (kTableBytes + (m + 1) * stride <= kMaxLds) {
+      panels = p;
+      break;
+    }
+  }
+  pl.panels = panels;
+  pl.kp = kb / panels;
+  pl.x_stride = pl.kp * 512 + 16;
+  int groups = cus / panels;
+  if (groups < 1) groups = 1;
+  pl.units = (int64_t)pl.tiles * pl.kp;
+  while (groups > 1 && (int64_t)groups * kWaves > pl.units) --groups;
+  pl.groups = groups;
+  const int64_t nw = (int64_t)groups * kWaves;
+  pl.nw = nw < pl.units ? nw : pl.units;
+  pl.maxc = (int)((pl.kp - 1) * pl.nw / pl.units) + 2;
+  // Dynamic LDS (x panel); the static table adds kTableBytes.
+  const int need = (m + 1) * pl.x_stride;
+  pl.lds_bytes = need + kTableBytes > kMinLds ? need : kMinLds - kTableBytes;
+  return pl;
+}
+
+struct DeviceState {
+  int cus = 0;
+  bool lds_attr_set[3] = {false, false, false};
+};
+
+struct Workspace {
+  float *ws = nullptr;
+  size_t ws_floats = 0;
+  uint32_t *counters = nullptr;
+  size_t ncounters = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+template <int BITS>
+const void *prefill_fn() {
+  return reinterpret_cast<const void *>(&prefill_kernel<BITS, Mix<BITS>::kMask>);
+}
+
+trellis_status device_state(DeviceState *&st, int bits) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
+  DeviceState &d = g_dev[dev];
+  if (d.cus == 0) {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || d.cus <= 0)
+      return TRELLIS_E_HIP;
+  }
+  if (!d.lds_attr_set[bits - 2]) {
+    const void *fn = bits == 2 ? prefill_fn<2>() : bits == 3 ? prefill_fn<3>() : prefill_fn<4>();
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - kTableBytes) != hipSuccess)
+      return TRELLIS_E_HIP;
+    d.lds_attr_set[bits - 2] = true;
+  }
+  st = &d;
+  return TRELLIS_OK;
+}
+
+// Per (device, stream) workspace: partial tiles and self-resetting counters.
+// Grown on demand and kept until process exit; a grown-out buffer is not
+// freed because earlier launches on the stream may still be using it.
+trellis_status workspace(hipStream_t stream, size_t ws_floats, size_t ncounters, Workspace *&out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
+  Workspace &w = g_ws[{dev, stream}];
+  if (w.ws_floats < ws_floats) {
+    float *p = nullptr;
+    if (hipMalloc(&p, ws_floats * sizeof(float)) != hipSuccess) return TRELLIS_E_HIP;
+    w.ws = p;
+    w.ws_floats = ws_floats;
+  }
+  if (w.ncounters < ncounters) {
+    uint32_t *c = nullptr;
+    if (hipMalloc(&c, ncounters * sizeof(uint32_t)) != hipSuccess) return TRELLIS_E_HIP;
+    if (hipMemsetAsync(c, 0, ncounters * sizeof(uint32_t), stream) != hipSuccess) return TRELLIS_E_HIP;
+    w.counters = c;
+    w.ncounters = ncounters;
+  }
+  out = &w;
+  return TRELLIS_OK;
+}
+
+}  // namespace
+}  // namespace trellis
+
+using namespace trellis;
+
+extern "C" {
+
+int trellis_supported(trellis_geom g, int32_t m) {
+  return geometry_ok(g) && m >= TRELLIS_MIN_M && m <= TRELLIS_MAX_M;
+}
+
+const char *trellis_status_string(trellis_status s) {
+  switch (s) {
+    case TRELLIS_OK: return "ok";
+    case TRELLIS_E_GEOMETRY: return "unsupported geometry (need t=256, l=12, bits 2/3/4, K%256==0, N%4==0)";
+    case TRELLIS_E_M: return "unsupported batch: m must be in [5, 15]";
+    case TRELLIS_E_NULL: return "null pointer argument";
+    case TRELLIS_E_ALIGN: return "misaligned pointer argument";
+    case TRELLIS_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16, trellis_geom g,
+                              uint16_t *w_bf16, void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (!codes || !scales_bf16 || !w_bf16) return TRELLIS_E_NULL;
+  if (!aligned(codes, 16) || !aligned(w_bf16, 16) || !aligned(scales_bf16, 2)) return TRELLIS_E_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int64_t threads = (int64_t)g.n * (g.k / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  clear_last_error();
+  switch (g.bits) {
+    case 2: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, stream, codes, scales_bf16, g.n, g.k, w_bf16); break;
+    case 3: hipLaunchKernelGGL(decode_kernel<3>, grid, block, 0, stream, codes, scales_bf16, g.n, g.k, w_bf16); break;
+    default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, stream, codes, scales_bf16, g.n, g.k, w_bf16); break;
+  }
+  return launch_status();
+}
+
+trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                               const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16,
+                               void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (m < TRELLIS_MIN_M || m > TRELLIS_MAX_M) return TRELLIS_E_M;
+  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16) return TRELLIS_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
+    return TRELLIS_E_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState *st = nullptr;
+  trellis_status rc = device_state(st, g.bits);
+  if (rc != TRELLIS_OK) return rc;
+  const Plan pl = make_plan(m, g.n, g.k, st->cus);
+  Workspace *w = nullptr;
+  rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256, (size_t)pl.tiles, w);
+  if (rc != TRELLIS_OK) return rc;
+  const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
+  clear_last_error();
+  switch (g.bits) {
+    case 2:
+      hipLaunchKernelGGL((prefill_kernel<2, Mix<2>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
+                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+      break;
+    case 3:
+      hipLaunchKernelGGL((prefill_kernel<3, Mix<3>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
+                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+      break;
+    default:
+      hipLaunchKernelGGL((prefill_kernel<4, Mix<4>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
+                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+      break;
+  }
+  return launch_status();
+}
+
+}  // extern "C"
