@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident codes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-passes", type=int, default=2)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -93,6 +95,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration_mb:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings calibrate the prefill kernel's measured HBM traffic.
+        nbytes = args.copy_calibration_mb << 20
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "launches": max(1, args.steps)}), flush=True)
+        return
 
     import trellis_coded_bit_prefill_amd as tp
     from workloads import SHAPES, generate_shape

@@ -117,3 +117,16 @@ def test_prefill_rejects_bad_m_on_device():
     x16 = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         tp.prefill(x16, codes, scales, 4)
+
+
+def test_prefill_k_panels_with_whole_tiles_per_wave():
+    # M=15 and K=5120 need two K panels of x in LDS; with N=65536 each wave's
+    # unit range spans whole tiles, which must still be summed across panels.
+    m, k, n, bits = 15, 5120, 65536, 2
+    print(f"prefill panels+whole tiles m={m} k={k} n={n}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=4200)
+    out = gpu_prefill(x, codes, scales, bits)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([np.arange(48), np.arange(n - 48, n), rng.integers(0, n, 256)]))
+    y, a = oracle.prefill_rows(x, codes, scales, k, bits, rows)
+    assert_prefill_close(out[:, rows], y, a, "panels+whole tiles")

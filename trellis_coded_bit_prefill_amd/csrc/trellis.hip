@@ -38,11 +38,13 @@ namespace trellis {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;                  // waves per prefill workgroup
+constexpr int kWaves = 12;                 // waves per prefill workgroup (3 per SIMD)
 constexpr int kWgThreads = kWave * kWaves;
 constexpr int kTableBytes = 4096 * 4;      // window -> float value
 constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
+constexpr int kStageRegs = 12;             // x-staging vectors (16 B) per thread
+static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - kTableBytes, "x staging must cover the largest panel");
 
 // ---------------------------------------------------------------------------
 // trellis_decode: W[N, K] bf16. One thread per 8 consecutive weights of one
@@ -183,32 +185,23 @@ __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, 
   }
 }
 
-// Finish a tile: sole contributor writes bf16 directly; otherwise publish the
-// partial and let the last arriving contributor add all partials in slot
-// order (fixed, so the result does not depend on arrival order).
-//
-// Cross-CU visibility without cache-wide maintenance: partials are written
-// and read with agent-scope relaxed atomics (coherent at the device level,
-// across the per-XCD L2s), and every lane's stores are complete
-// (s_waitcnt vmcnt(0)) before lane 0 bumps the tile counter. The last
-// arriver's loads are issued only after its counter update returned, so
-// they observe every published partial. A full __threadfence() would write
-// back and invalidate the whole L2 at each flush instead.
-__device__ __forceinline__ void flush_tile(const Plan &pl, int tile, int panel, int64_t wave_id, int64_t nw,
-                                        f32x4 acc, float *__restrict__ ws, uint32_t *__restrict__ counters,
-                                        uint16_t *__restrict__ out, int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  const int row = tile * 16 + j;
-  const int64_t first = (int64_t)tile * pl.kp;
-  const int64_t o0 = owner_of(first, nw, pl.units);
-  const int64_t o1 = owner_of(first + pl.kp - 1, nw, pl.units);
-  const int contrib = (int)(o1 - o0 + 1);
+// First unit of wave w's range (floor partition of the panel's units).
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t nw, int64_t units) { return w * units / nw; }
+
+// Cross-CU completion of a tile whose units are split between workgroups.
+// The CU's partial is written with agent-scope relaxed atomic stores
+// (coherent across the per-XCD L2s) and every lane's stores are complete
+// (s_waitcnt vmcnt(0)) before lane 0 bumps the tile counter; the last
+// arriving contributor -- whose loads are issued only after its counter
+// update returned -- adds all partials in slot order (fixed, so the result
+// does not depend on arrival order), stores bf16 and resets the counter.
+// No cache-wide fence (L2 writeback/invalidate) is needed.
+__device__ __forceinline__ void finish_shared_tile(const Plan &pl, int tile, int panel, int slot_idx, int contrib,
+                                                   f32x4 acc, float *__restrict__ ws,
+                                                   uint32_t *__restrict__ counters, uint16_t *__restrict__ out,
+                                                   int lane) {
   const int total = contrib * pl.panels;
-  if (total == 1) {
-    store_tile(out, acc, pl.m, pl.n, row, g);
-    return;
-  }
-  float *slot = ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + (wave_id - o0)) * 256 + 4 * lane;
+  float *slot = ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + slot_idx) * 256 + 4 * lane;
 #pragma unroll
   for (int e = 0; e < 4; ++e) __hip_atomic_store(slot + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -223,7 +216,7 @@ __device__ __forceinline__ void flush_tile(const Plan &pl, int tile, int panel, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) sum[e] += __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-  store_tile(out, sum, pl.m, pl.n, row, g);
+  store_tile(out, sum, pl.m, pl.n, tile * 16 + (lane & 15), lane >> 4);
   if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -235,78 +228,202 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
                                                              uint32_t *__restrict__ counters, Plan pl) {
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
+  // After the main loop the x region is reused for the waves' partial tiles.
   __shared__ __attribute__((aligned(16))) float s_table[4096];
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
   unsigned char *const xl = lds;
   constexpr int wpb = 8 * BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int j = lane & 15, g = lane >> 4;
   const int panel = blockIdx.x % pl.panels;
   const int group = blockIdx.x / pl.panels;
   const int panel_k = pl.kp * 256;
   const int64_t kbase = (int64_t)panel * panel_k;
+  const int64_t row_words = (int64_t)(pl.k >> 8) * wpb;
 
-  // Stage x[:, panel] (M rows) and an all-zero row M.
-  const int vecs = panel_k / 8;
-  for (int v = tid; v < (pl.m + 1) * vecs; v += kWgThreads) {
-    const int i = v / vecs, c = v - i * vecs;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (i < pl.m) val = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
-    *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = val;
-  }
-  // Window -> value table, by the page's arithmetic.
-  for (int e = tid; e < 4096; e += kWgThreads) s_table[e] = trellis_value(code_of((uint32_t)e));
-  __syncthreads();
-
-  const int j = lane & 15, g = lane >> 4;
   // Every active wave gets a non-empty range because nw <= units; waves
   // beyond nw (tiny problems only) have nothing to do.
   const int64_t nw = pl.nw;
   const int64_t wave_id = (int64_t)group * kWaves + wave;
-  const int64_t u0 = wave_id < nw ? wave_id * pl.units / nw : 0;
-  const int64_t u1 = wave_id < nw ? (wave_id + 1) * pl.units / nw : 0;
-  const int64_t row_words = (int64_t)(pl.k >> 8) * wpb;
-  const unsigned char *xa = xl + (j < pl.m ? j : pl.m) * pl.x_stride + (192 - 64 * g) * 2;
+  const bool active = wave_id < nw;
+  const int64_t u0 = active ? range_start(wave_id, nw, pl.units) : 0;
+  const int64_t u1 = active ? range_start(wave_id + 1, nw, pl.units) : 0;
 
-  int cur = -1;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float s = 0.f, q = 0.f;
-  bool table_only = false;
-  const uint32_t *rowp = codes;
-  bool row_ok = false;
-  // (tile, b) of unit u0, then stepped without dividing.
+  // Rows past N (last tile only) read row 0's words and get scale 0, so
+  // their weights are zero and their outputs are never stored.
+  auto unit_words = [&](int t, int bb) {
+    const int row = t * 16 + j;
+    return codes + (int64_t)(row < pl.n ? row : 0) * row_words + ((int64_t)panel * pl.kp + bb) * wpb;
+  };
+  // Raw scale bits of this lane's row in tile t (row 0's for rows past N);
+  // converted only when the tile starts, so the load is not waited for early.
+  auto tile_scale_bits = [&](int t) -> uint32_t {
+    const int row = t * 16 + j;
+    return scales[row < pl.n ? row : 0];
+  };
+  auto scale_of = [&](int t, uint32_t bits) { return t * 16 + j < pl.n ? bf16_bits_to_f32((uint16_t)bits) : 0.f; };
+
+  // Prologue. x[:, panel] (M rows and an all-zero row M) is loaded and
+  // stored to LDS first, while the window -> value table is built; only then
+  // are code words requested, so the x loads do not queue behind every
+  // wave's burst of code-stream requests.
+  const int vecs = panel_k / 8;
+  const int xtotal = (pl.m + 1) * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
+  {
+    uint4 xv[kStageRegs];
+#pragma unroll
+    for (int r = 0; r < kStageRegs; ++r) {
+      const int idx = r * kWgThreads + tid;
+      xv[r] = uint4{0u, 0u, 0u, 0u};
+      if (idx < xtotal) {
+        const int i = idx / vecs, c = idx - i * vecs;
+        if (i < pl.m) xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
+      }
+    }
+    for (int e = tid; e < 4096; e += kWgThreads) s_table[e] = trellis_value(code_of((uint32_t)e));
+#pragma unroll
+    for (int r = 0; r < kStageRegs; ++r) {
+      const int idx = r * kWgThreads + tid;
+      if (idx < xtotal) {
+        const int i = idx / vecs, c = idx - i * vecs;
+        *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = xv[r];
+      }
+    }
+  }
+
+  // Code words (and the row scale) of each unit live in one of three
+  // register slots: the unit being decoded and the next two in flight. The
+  // loop below is unrolled by three so the slots rotate without copying
+  // registers that still have loads pending.
+  struct Slot {
+    LaneWords<BITS> w;
+    uint32_t scb;  // raw bf16 scale bits
+  };
+  Slot S0, S1, S2;
   int tile = (int)(u0 / pl.kp);
   int b = (int)(u0 - (int64_t)tile * pl.kp);
-  for (int64_t u = u0; u < u1; ++u, ++b) {
-    if (b == pl.kp) {
-      b = 0;
-      ++tile;
+  int pt = tile, pb = b;  // next unit to request
+  auto advance = [&](int &t, int &bb) {
+    if (++bb == pl.kp) {
+      bb = 0;
+      ++t;
     }
-    if (tile != cur) {
-      if (cur >= 0) flush_tile(pl, cur, panel, wave_id, nw, acc, ws, counters, out, lane);
-      cur = tile;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = tile * 16 + j;
-      row_ok = row < pl.n;
-      s = row_ok ? bf16_bits_to_f32(scales[row]) : 0.f;
-      q = s * kR;
-      table_only = !__all(alu_scale_ok(s));
-      rowp = codes + (int64_t)(row_ok ? row : 0) * row_words + (int64_t)panel * pl.kp * wpb;
+  };
+  auto request = [&](Slot &S) {
+    load_words<BITS>(unit_words(pt, pb), g, S.w);
+    S.scb = tile_scale_bits(pt);
+    advance(pt, pb);
+  };
+  // Requests are unconditional (straight-line code keeps the compiler's
+  // memory-counter waits exact); past the end of the range they read valid,
+  // cache-resident words that are never decoded.
+  request(S0);
+  request(S1);
+  __syncthreads();
+
+  const unsigned char *xa = xl + (j < pl.m ? j : pl.m) * pl.x_stride + (192 - 64 * g) * 2;
+
+  // Tiles of this wave: the first may be shared with earlier waves and the
+  // last with later ones (both kept as partials until the end); complete
+  // tiles are stored as soon as they are done.
+  const int tf = (int)(u0 / pl.kp);
+  f32x4 part_f = {0.f, 0.f, 0.f, 0.f}, part_l = {0.f, 0.f, 0.f, 0.f};
+  // A tile whose units (of this panel) all lie in this wave: final when x
+  // has one panel; otherwise this wave is the panel's only contributor.
+  auto complete_tile = [&](int t, f32x4 v) {
+    if (pl.panels == 1) store_tile(out, v, pl.m, pl.n, t * 16 + j, g);
+    else finish_shared_tile(pl, t, panel, 0, 1, v, ws, counters, out, lane);
+  };
+  if (u0 < u1) {
+    int cur = tile;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float s = scale_of(tile, S0.scb), q = s * kR;
+    bool table_only = !__all(alu_scale_ok(s));
+    int64_t u = u0;
+    // Decode unit u from slot C while unit u + 2 is requested into slot N.
+    auto step = [&](Slot &C, Slot &N) {
+      if (tile != cur) {
+        // tile `cur` is done; only the range's first tile can be shared here
+        if (cur == tf && u0 > (int64_t)tf * pl.kp) part_f = acc;
+        else complete_tile(cur, acc);
+        cur = tile;
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        s = scale_of(tile, C.scb);
+        q = s * kR;
+        table_only = !__all(alu_scale_ok(s));
+      }
+      request(N);
+      const unsigned char *xb = xa + b * 512;
+      if (table_only)
+        unit<BITS, 0xFF>(C.w, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+      else
+        unit<BITS, MASK>(C.w, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+      advance(tile, b);
+      ++u;
+    };
+    for (;;) {
+      step(S0, S2);
+      if (u == u1) break;
+      step(S1, S0);
+      if (u == u1) break;
+      step(S2, S1);
+      if (u == u1) break;
     }
-    LaneWords<BITS> L;
-    if (row_ok) {
-      load_words<BITS>(rowp + (int64_t)b * wpb, g, L);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2 * BITS + 1; ++i) L.d[i] = 0u;
-    }
-    const unsigned char *xb = xa + b * 512;
-    if (table_only)
-      unit<BITS, 0xFF>(L, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
-    else
-      unit<BITS, MASK>(L, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+    // the range's last tile
+    if (u0 <= (int64_t)cur * pl.kp && u1 == (int64_t)(cur + 1) * pl.kp) complete_tile(cur, acc);
+    else if (cur == tf) part_f = acc;
+    else part_l = acc;
   }
-  if (cur >= 0) flush_tile(pl, cur, panel, wave_id, nw, acc, ws, counters, out, lane);
+
+  // ---- Combine shared tiles: within the CU through LDS, across CUs through
+  // the workspace. Wave w holds a partial of its first tile when its range
+  // does not cover that whole tile, and a partial of its last tile (when
+  // different) when its range ends inside it.
+  __syncthreads();  // all waves are done reading x; its LDS holds the partials now
+  f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [wave][first, last][lane]
+  slots[(wave * 2 + 0) * kWave + lane] = part_f;
+  slots[(wave * 2 + 1) * kWave + lane] = part_l;
+  __syncthreads();
+  if (!active) return;
+
+  const int64_t cu_w0 = (int64_t)group * kWaves;                     // first wave of this CU
+  const int64_t cu_w1 = cu_w0 + kWaves < nw ? cu_w0 + kWaves : nw;  // one past its last active wave
+  const int64_t cu_u0 = range_start(cu_w0, nw, pl.units), cu_u1 = range_start(cu_w1, nw, pl.units);
+  // The wave leads each shared tile of its range that no earlier wave of the
+  // CU holds, and adds the CU's partials of it in wave order.
+  for (int which = 0; which < 2; ++which) {
+    int64_t T;
+    if (which == 0) {
+      T = u0 / pl.kp;
+      if (u0 == T * pl.kp && u1 >= (T + 1) * pl.kp) continue;  // complete in this wave
+      if (wave_id > cu_w0 && u0 > T * pl.kp) continue;          // an earlier wave of the CU holds T
+    } else {
+      T = (u1 - 1) / pl.kp;
+      if (T == u0 / pl.kp || u1 == (T + 1) * pl.kp) continue;  // same as the first, or complete
+    }
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t w = wave_id; w < cu_w1; ++w) {
+      const int64_t a = range_start(w, nw, pl.units), e = range_start(w + 1, nw, pl.units);
+      int which_slot;
+      if (a / pl.kp == T) which_slot = 0;
+      else if ((e - 1) / pl.kp == T) which_slot = 1;
+      else break;
+      const f32x4 v = slots[((int)(w - cu_w0) * 2 + which_slot) * kWave + lane];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
+      if ((e - 1) / pl.kp != T) break;
+    }
+    const int64_t t0u = T * pl.kp, t1u = t0u + pl.kp;
+    if (t0u >= cu_u0 && t1u <= cu_u1 && pl.panels == 1) {
+      store_tile(out, sum, pl.m, pl.n, (int)T * 16 + j, g);
+    } else {
+      // CUs of this panel holding units of T, and this CU's index among them.
+      const int64_t c0 = owner_of(t0u, nw, pl.units) / kWaves;
+      const int64_t c1 = owner_of(t1u - 1, nw, pl.units) / kWaves;
+      finish_shared_tile(pl, (int)T, panel, (int)(group - c0), (int)(c1 - c0 + 1), sum, ws, counters, out, lane);
+    }
+  }
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
@@ -361,7 +478,14 @@ Plan make_plan(int m, int n, int k, int cus) {
   pl.groups = groups;
   const int64_t nw = (int64_t)groups * kWaves;
   pl.nw = nw < pl.units ? nw : pl.units;
-  pl.maxc = (int)((pl.kp - 1) * pl.nw / pl.units) + 2;
+  // Workgroups sharing one tile: at most (kp - 1) / (shortest CU range) + 2.
+  int64_t minlen = pl.units;
+  for (int64_t c = 0; c * kWaves < pl.nw; ++c) {
+    const int64_t w0 = c * kWaves, w1 = (c + 1) * kWaves < pl.nw ? (c + 1) * kWaves : pl.nw;
+    const int64_t len = w1 * pl.units / pl.nw - w0 * pl.units / pl.nw;
+    if (len < minlen) minlen = len;
+  }
+  pl.maxc = (int)((pl.kp - 1) / minlen) + 2;
   // Dynamic LDS (x panel); the static table adds kTableBytes.
   const int need = (m + 1) * pl.x_stride;
   pl.lds_bytes = need + kTableBytes > kMinLds ? need : kMinLds - kTableBytes;
