@@ -11,7 +11,8 @@ import pytest
 import oracle
 import trellis_coded_bit_prefill_amd as tp
 from workloads import SHAPES, generate, generate_shape
-from tests.helpers import assert_prefill_close, from_dev_bf16, to_dev_bf16, to_dev_codes
+from tests.helpers import (assert_prefill_close, exhaustive_window_codes, from_dev_bf16, to_dev_bf16,
+                           to_dev_codes)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +131,35 @@ def test_prefill_k_panels_with_whole_tiles_per_wave():
     rows = np.unique(np.concatenate([np.arange(48), np.arange(n - 48, n), rng.integers(0, n, 256)]))
     y, a = oracle.prefill_rows(x, codes, scales, k, bits, rows)
     assert_prefill_close(out[:, rows], y, a, "panels+whole tiles")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_prefill_weights_bit_exact_every_window_and_scale(bits):
+    # One-hot x rows pick single columns of W, so every output is one decoded
+    # weight (sum of one exact product): prefill's in-kernel decode (both the
+    # LDS-table and the ALU path) must give exactly the oracle's weights.
+    # Rows hold all 4096 windows; scales cover the 257 reachable values, both
+    # signs, zero, and magnitudes outside 2^-110..2^110 (table-only rows).
+    import torch
+
+    print(f"prefill one-hot exhaustive bits={bits}", flush=True)
+    rng = np.random.default_rng(600 + bits)
+    extra = [0x3F80, 0xBF80, 0xBC00, 0xBCA4, 0x0000, 0x8000, 0x0B00, 0x7300, 0x3FFF, 0xC07F,
+             0x0600, 0x7900, 0x8600]
+    scales = np.concatenate([np.arange(0x3BA4, 0x3CA5, dtype=np.uint16), np.array(extra, dtype=np.uint16)])
+    scales = np.concatenate([scales, np.full((-scales.size) % 16, 0x3C00, dtype=np.uint16)])
+    codes, k = exhaustive_window_codes(rng, scales.size, bits)
+    w_ref = oracle.decode(codes, scales, k, bits)
+    cd, sd = to_dev_codes(codes), to_dev_bf16(scales)
+    m = 15
+    bad = 0
+    for c0 in range(0, k, m):
+        cols = np.arange(c0, min(c0 + m, k))
+        x = np.zeros((max(5, cols.size), k), dtype=np.uint16)
+        x[np.arange(cols.size), cols] = 0x3F80
+        out = tp.prefill(to_dev_bf16(x), cd, sd, bits)
+        torch.cuda.synchronize()
+        got = (from_dev_bf16(out)[: cols.size].astype(np.uint32) << 16).view(np.float32)
+        ref = (w_ref[:, cols].T.astype(np.uint32) << 16).view(np.float32)
+        bad += int(np.sum(got != ref))  # +0 == -0: zero weights may differ in sign only
+    assert bad == 0

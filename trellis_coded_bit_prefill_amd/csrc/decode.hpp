@@ -49,6 +49,33 @@ __device__ __forceinline__ int code_of(uint32_t win) {
   return (int)__builtin_amdgcn_sad_u8(hash_1mad(win), 0u, 0xFFFFFE02u);
 }
 
+// 1.5*2^23 + code as a float: v_sad_u8 adds the byte sum to the bit pattern
+// 0x4B3FFE02 = bits(1.5*2^23) - 510, and 1.5*2^23 + code stays inside the
+// binade [2^23, 2^24) where the float spacing is 1.
+__device__ __forceinline__ float code_plus_magic(uint32_t win) {
+  return __uint_as_float(__builtin_amdgcn_sad_u8(hash_1mad(win), 0u, 0x4B3FFE02u));
+}
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+// ALU-path row constants: q = float32(s * r) rounded to the nearest multiple
+// of 4 units in its last place, so K = -1.5*2^23 * q is exact and
+// fma(1.5*2^23 + code, q, K) rounds code*q exactly once. For every code and
+// every bf16 scale mantissa (either sign) bf16(code * q) equals the page's
+// weight (zero weights may differ in sign only).
+__device__ __forceinline__ void alu_row_constants(float s, float &q, float &k) {
+  q = __uint_as_float((__float_as_uint(s * kR) + 2u) & ~3u);
+  k = -kMagic * q;
+}
+
+// (v >> 16) & m in one VALU op (SDWA word select on the first operand).
+__device__ __forceinline__ uint32_t and_hi16(uint32_t v, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(v), "v"(m));
+  return r;
+}
+
 // The page's normalisation: a = c*r, residual = fma(-a, C, c), a + residual*r.
 __device__ __forceinline__ float trellis_value(int code) {
   const float c = (float)code;
@@ -99,6 +126,36 @@ __device__ __forceinline__ uint32_t win_x4(const uint32_t (&D)[N]) {
   } else {
     return (D[w] << (2 - b)) & 0x3FFCu;
   }
+}
+
+// Table byte addresses (window * 4) of the four windows whose lowest bits
+// are at O0, O0+16, O0+32 and O0+48: two words holding stream bits
+// [O0-2, O0+62) are built once, and each address is one mask of their low or
+// high halves (mask = 0x3FFC in a register, for the SDWA form).
+template <int O0, int N>
+__device__ __forceinline__ void quad_x4(const uint32_t (&D)[N], uint32_t mask, uint32_t (&a)[4]) {
+  constexpr int sh = O0 - 2;
+  uint32_t lo, hi;
+  if constexpr (sh < 0) {
+    static_assert(sh == -2 || sh == -1, "unexpected window offset");
+    lo = D[0] << (-sh);
+    hi = __builtin_amdgcn_alignbit(D[1], D[0], 32 + sh);
+  } else {
+    constexpr int w = sh >> 5, r = sh & 31;
+    if constexpr (r == 0) {
+      static_assert(w + 1 < N, "quad outside the lane's words");
+      lo = D[w];
+      hi = D[w + 1];
+    } else {
+      static_assert(w + 2 < N, "quad outside the lane's words");
+      lo = __builtin_amdgcn_alignbit(D[w + 1], D[w], r);
+      hi = __builtin_amdgcn_alignbit(D[w + 2], D[w + 1], r);
+    }
+  }
+  a[0] = lo & 0x3FFCu;
+  a[1] = and_hi16(lo, mask);
+  a[2] = hi & 0x3FFCu;
+  a[3] = and_hi16(hi, mask);
 }
 
 }  // namespace trellis

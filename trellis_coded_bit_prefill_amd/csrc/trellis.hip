@@ -92,13 +92,23 @@ struct Plan {
   int32_t maxc;      // contributor slots per (tile, panel) in the workspace
   int32_t x_stride;  // bytes per staged x row
   int32_t lds_bytes;
-  int64_t units;     // tiles * kp (per panel)
-  int64_t nw;        // active waves per panel: min(groups * waves, units)
+  int32_t units;     // tiles * kp (per panel), < 2^28
+  int32_t nw;        // active waves per panel: min(groups * waves, units)
+  int32_t base;      // units / nw: every active wave gets base or base + 1 units
+  int32_t rem;       // units % nw: the first rem waves get base + 1
+  uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
 };
 
-__device__ __forceinline__ int64_t owner_of(int64_t u, int64_t nw, int64_t units) {
-  // The wave whose range [floor(w*U/V), floor((w+1)*U/V)) holds unit u.
-  return ((u + 1) * nw - 1) / units;
+// First unit of active wave w: waves 0..rem-1 hold base + 1 units, the rest
+// base units, in order.
+__device__ __forceinline__ int range_start(int w, const Plan &pl) {
+  return w * pl.base + (w < pl.rem ? w : pl.rem);
+}
+
+// The active wave whose range holds unit u.
+__device__ __forceinline__ int owner_of(int u, const Plan &pl) {
+  const int cut = pl.rem * (pl.base + 1);
+  return u < cut ? u / (pl.base + 1) : pl.rem + (u - cut) / pl.base;
 }
 
 // Lane (j, g) of a wave: j = row of the 16-row tile (B column) and x row (A
@@ -149,31 +159,111 @@ __device__ __forceinline__ bf16x8 group_table(const LaneWords<BITS> &L, const un
 }
 
 template <int BITS, int U, int... S>
-__device__ __forceinline__ bf16x8 group_alu(const LaneWords<BITS> &L, float q, std::integer_sequence<int, S...>) {
-  const float f[8] = {((float)code_of(win12<(63 - 8 * U - S) * BITS>(L.d)) * q)...};
+__device__ __forceinline__ bf16x8 group_alu(const LaneWords<BITS> &L, float q, float k,
+                                            std::integer_sequence<int, S...>) {
+  const float f[8] = {__builtin_fmaf(code_plus_magic(win12<(63 - 8 * U - S) * BITS>(L.d)), q, k)...};
   bf16x8 w;
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
   return w;
 }
 
-// One unit: 8 MFMA groups over the lane's 64 weights of one block.
+// Table-path groups sharing window extraction. Windows 16 bits apart come
+// out of one pair of shifted words (quad_x4): for k = 4 they are 4 weights
+// apart, so groups (U, U+1) share four quads; for k = 2 they are 8 weights
+// apart, so groups U..U+3 share eight quads.
+template <int BITS, int U>
+__device__ __forceinline__ void table_span(const LaneWords<BITS> &L, const unsigned char *table, float s,
+                                           uint32_t mask, bf16x8 *w) {
+  static_assert(BITS == 4 || BITS == 2, "spans exist for k = 4 and k = 2");
+  constexpr int G = BITS == 4 ? 2 : 4;  // groups in the span
+  constexpr int Q = 8 * G / 4;          // quads in the span
+  float f[G][8];
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    uint32_t a[4];
+    if constexpr (BITS == 4) {
+      // idx = 8U + s' + {12, 8, 4, 0}, s' = i (0..3): (group U+1, slot 4+s'),
+      // (U+1, s'), (U, 4+s'), (U, s')
+      switch (i) {
+        case 0: quad_x4<(63 - (8 * U + 12 + 0)) * 4>(L.d, mask, a); break;
+        case 1: quad_x4<(63 - (8 * U + 12 + 1)) * 4>(L.d, mask, a); break;
+        case 2: quad_x4<(63 - (8 * U + 12 + 2)) * 4>(L.d, mask, a); break;
+        default: quad_x4<(63 - (8 * U + 12 + 3)) * 4>(L.d, mask, a); break;
+      }
+      f[1][4 + i] = lds_table(table, a[0]) * s;
+      f[1][i] = lds_table(table, a[1]) * s;
+      f[0][4 + i] = lds_table(table, a[2]) * s;
+      f[0][i] = lds_table(table, a[3]) * s;
+    } else {
+      // idx = 8U + s' + {24, 16, 8, 0}, s' = i (0..7): groups U+3, U+2, U+1, U at slot s'
+      switch (i) {
+        case 0: quad_x4<(63 - (8 * U + 24 + 0)) * 2>(L.d, mask, a); break;
+        case 1: quad_x4<(63 - (8 * U + 24 + 1)) * 2>(L.d, mask, a); break;
+        case 2: quad_x4<(63 - (8 * U + 24 + 2)) * 2>(L.d, mask, a); break;
+        case 3: quad_x4<(63 - (8 * U + 24 + 3)) * 2>(L.d, mask, a); break;
+        case 4: quad_x4<(63 - (8 * U + 24 + 4)) * 2>(L.d, mask, a); break;
+        case 5: quad_x4<(63 - (8 * U + 24 + 5)) * 2>(L.d, mask, a); break;
+        case 6: quad_x4<(63 - (8 * U + 24 + 6)) * 2>(L.d, mask, a); break;
+        default: quad_x4<(63 - (8 * U + 24 + 7)) * 2>(L.d, mask, a); break;
+      }
+      f[3][i] = lds_table(table, a[0]) * s;
+      f[2][i] = lds_table(table, a[1]) * s;
+      f[1][i] = lds_table(table, a[2]) * s;
+      f[0][i] = lds_table(table, a[3]) * s;
+    }
+  }
+#pragma unroll
+  for (int gidx = 0; gidx < G; ++gidx)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[gidx][e] = (__bf16)f[gidx][e];
+}
+
+// Decode-path choice per MFMA group: bit u of MASK set = table path.
+// Spans (k = 4: aligned pairs, k = 2: aligned quads) whose groups all use
+// the table path share window extraction.
+template <int BITS, int MASK, int U>
+constexpr bool span_start() {
+  if constexpr (BITS == 4) return U % 2 == 0 && ((MASK >> U) & 3) == 3;
+  else if constexpr (BITS == 2) return U % 4 == 0 && ((MASK >> U) & 15) == 15;
+  else return false;
+}
+template <int BITS, int MASK, int U>
+constexpr bool in_span() {
+  if constexpr (BITS == 4) return span_start<BITS, MASK, U - U % 2>();
+  else if constexpr (BITS == 2) return span_start<BITS, MASK, U - U % 4>();
+  else return false;
+}
+
 template <int BITS, int MASK, int U>
 __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsigned char *table,
-                                           const unsigned char *xa, float s, float q, f32x4 &acc) {
-  bf16x8 w;
-  if constexpr ((MASK >> U) & 1)
-    w = group_table<BITS, U>(L, table, s, std::make_integer_sequence<int, 8>{});
-  else
-    w = group_alu<BITS, U>(L, q, std::make_integer_sequence<int, 8>{});
-  const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+                                           const unsigned char *xa, float s, float q, float k, uint32_t mask,
+                                           f32x4 &acc) {
+  if constexpr (span_start<BITS, MASK, U>()) {
+    constexpr int G = BITS == 4 ? 2 : 4;
+    bf16x8 w[G];
+    table_span<BITS, U>(L, table, s, mask, w);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * (U + i));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w[i], acc, 0, 0, 0);
+    }
+  } else if constexpr (!in_span<BITS, MASK, U>()) {
+    bf16x8 w;
+    if constexpr ((MASK >> U) & 1)
+      w = group_table<BITS, U>(L, table, s, std::make_integer_sequence<int, 8>{});
+    else
+      w = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
+    const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+  }
 }
 
 template <int BITS, int MASK, int... U>
 __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned char *table, const unsigned char *xa,
-                                     float s, float q, f32x4 &acc, std::integer_sequence<int, U...>) {
-  (unit_group<BITS, MASK, U>(L, table, xa, s, q, acc), ...);
+                                     float s, float q, float k, uint32_t mask, f32x4 &acc,
+                                     std::integer_sequence<int, U...>) {
+  (unit_group<BITS, MASK, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
 __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
@@ -184,9 +274,6 @@ __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, 
     if (i < m) out[(int64_t)i * n + row] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
   }
 }
-
-// First unit of wave w's range (floor partition of the panel's units).
-__device__ __forceinline__ int64_t range_start(int64_t w, int64_t nw, int64_t units) { return w * units / nw; }
 
 // Cross-CU completion of a tile whose units are split between workgroups.
 // The CU's partial is written with agent-scope relaxed atomic stores
@@ -244,11 +331,11 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
 
   // Every active wave gets a non-empty range because nw <= units; waves
   // beyond nw (tiny problems only) have nothing to do.
-  const int64_t nw = pl.nw;
-  const int64_t wave_id = (int64_t)group * kWaves + wave;
+  const int nw = pl.nw;
+  const int wave_id = group * kWaves + wave;
   const bool active = wave_id < nw;
-  const int64_t u0 = active ? range_start(wave_id, nw, pl.units) : 0;
-  const int64_t u1 = active ? range_start(wave_id + 1, nw, pl.units) : 0;
+  const int u0 = active ? range_start(wave_id, pl) : 0;
+  const int u1 = active ? range_start(wave_id + 1, pl) : 0;
 
   // Rows past N (last tile only) read row 0's words and get scale 0, so
   // their weights are zero and their outputs are never stored.
@@ -277,7 +364,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       const int idx = r * kWgThreads + tid;
       xv[r] = uint4{0u, 0u, 0u, 0u};
       if (idx < xtotal) {
-        const int i = idx / vecs, c = idx - i * vecs;
+        const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
         if (i < pl.m) xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
       }
     }
@@ -286,7 +373,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     for (int r = 0; r < kStageRegs; ++r) {
       const int idx = r * kWgThreads + tid;
       if (idx < xtotal) {
-        const int i = idx / vecs, c = idx - i * vecs;
+        const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
         *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = xv[r];
       }
     }
@@ -302,7 +389,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   };
   Slot S0, S1, S2;
   int tile = (int)(u0 / pl.kp);
-  int b = (int)(u0 - (int64_t)tile * pl.kp);
+  int b = u0 - tile * pl.kp;
   int pt = tile, pb = b;  // next unit to request
   auto advance = [&](int &t, int &bb) {
     if (++bb == pl.kp) {
@@ -338,27 +425,29 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   if (u0 < u1) {
     int cur = tile;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float s = scale_of(tile, S0.scb), q = s * kR;
+    float s = scale_of(tile, S0.scb), q, kq;
+    alu_row_constants(s, q, kq);
     bool table_only = !__all(alu_scale_ok(s));
-    int64_t u = u0;
+    const uint32_t mask3ffc = 0x3FFCu;
+    int u = u0;
     // Decode unit u from slot C while unit u + 2 is requested into slot N.
     auto step = [&](Slot &C, Slot &N) {
       if (tile != cur) {
         // tile `cur` is done; only the range's first tile can be shared here
-        if (cur == tf && u0 > (int64_t)tf * pl.kp) part_f = acc;
+        if (cur == tf && u0 > tf * pl.kp) part_f = acc;
         else complete_tile(cur, acc);
         cur = tile;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
         s = scale_of(tile, C.scb);
-        q = s * kR;
+        alu_row_constants(s, q, kq);
         table_only = !__all(alu_scale_ok(s));
       }
       request(N);
       const unsigned char *xb = xa + b * 512;
       if (table_only)
-        unit<BITS, 0xFF>(C.w, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, 0xFF>(C.w, table, xb, s, q, kq, mask3ffc, acc, std::make_integer_sequence<int, 8>{});
       else
-        unit<BITS, MASK>(C.w, table, xb, s, q, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, MASK>(C.w, table, xb, s, q, kq, mask3ffc, acc, std::make_integer_sequence<int, 8>{});
       advance(tile, b);
       ++u;
     };
@@ -371,7 +460,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       if (u == u1) break;
     }
     // the range's last tile
-    if (u0 <= (int64_t)cur * pl.kp && u1 == (int64_t)(cur + 1) * pl.kp) complete_tile(cur, acc);
+    if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) complete_tile(cur, acc);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
@@ -387,13 +476,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   __syncthreads();
   if (!active) return;
 
-  const int64_t cu_w0 = (int64_t)group * kWaves;                     // first wave of this CU
-  const int64_t cu_w1 = cu_w0 + kWaves < nw ? cu_w0 + kWaves : nw;  // one past its last active wave
-  const int64_t cu_u0 = range_start(cu_w0, nw, pl.units), cu_u1 = range_start(cu_w1, nw, pl.units);
+  const int cu_w0 = group * kWaves;                              // first wave of this CU
+  const int cu_w1 = cu_w0 + kWaves < nw ? cu_w0 + kWaves : nw;  // one past its last active wave
+  const int cu_u0 = range_start(cu_w0, pl), cu_u1 = range_start(cu_w1, pl);
   // The wave leads each shared tile of its range that no earlier wave of the
   // CU holds, and adds the CU's partials of it in wave order.
   for (int which = 0; which < 2; ++which) {
-    int64_t T;
+    int T;
     if (which == 0) {
       T = u0 / pl.kp;
       if (u0 == T * pl.kp && u1 >= (T + 1) * pl.kp) continue;  // complete in this wave
@@ -403,8 +492,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       if (T == u0 / pl.kp || u1 == (T + 1) * pl.kp) continue;  // same as the first, or complete
     }
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t w = wave_id; w < cu_w1; ++w) {
-      const int64_t a = range_start(w, nw, pl.units), e = range_start(w + 1, nw, pl.units);
+    for (int w = wave_id; w < cu_w1; ++w) {
+      const int a = range_start(w, pl), e = range_start(w + 1, pl);
       int which_slot;
       if (a / pl.kp == T) which_slot = 0;
       else if ((e - 1) / pl.kp == T) which_slot = 1;
@@ -414,13 +503,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
       if ((e - 1) / pl.kp != T) break;
     }
-    const int64_t t0u = T * pl.kp, t1u = t0u + pl.kp;
+    const int t0u = T * pl.kp, t1u = t0u + pl.kp;
     if (t0u >= cu_u0 && t1u <= cu_u1 && pl.panels == 1) {
       store_tile(out, sum, pl.m, pl.n, (int)T * 16 + j, g);
     } else {
       // CUs of this panel holding units of T, and this CU's index among them.
-      const int64_t c0 = owner_of(t0u, nw, pl.units) / kWaves;
-      const int64_t c1 = owner_of(t1u - 1, nw, pl.units) / kWaves;
+      const int c0 = owner_of(t0u, pl) / kWaves;
+      const int c1 = owner_of(t1u - 1, pl) / kWaves;
       finish_shared_tile(pl, (int)T, panel, (int)(group - c0), (int)(c1 - c0 + 1), sum, ws, counters, out, lane);
     }
   }
@@ -429,9 +518,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
 // use ALU arithmetic.
 template <int BITS> struct Mix;
-template <> struct Mix<2> { static constexpr int kMask = 0b01011011; };
+template <> struct Mix<2> { static constexpr int kMask = 0b00001111; };
 template <> struct Mix<3> { static constexpr int kMask = 0b01011011; };
-template <> struct Mix<4> { static constexpr int kMask = 0b01011011; };
+template <> struct Mix<4> { static constexpr int kMask = 0b00110111; };
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -471,18 +560,27 @@ Plan make_plan(int m, int n, int k, int cus) {
   pl.panels = panels;
   pl.kp = kb / panels;
   pl.x_stride = pl.kp * 512 + 16;
+  // Staging divides a vector index (< 2^14) by the vectors per row
+  // (kp * 32 >= 32): umulhi(i, ceil(2^32 / d)) is exact while i * d < 2^32.
+  {
+    const uint64_t d = (uint64_t)pl.kp * 32;
+    pl.xdiv = (uint32_t)(((1ull << 32) + d - 1) / d);
+  }
   int groups = cus / panels;
   if (groups < 1) groups = 1;
-  pl.units = (int64_t)pl.tiles * pl.kp;
-  while (groups > 1 && (int64_t)groups * kWaves > pl.units) --groups;
+  pl.units = pl.tiles * pl.kp;  // <= 2^18 tiles * 2^10 blocks
+  while (groups > 1 && groups * kWaves > pl.units) --groups;
   pl.groups = groups;
-  const int64_t nw = (int64_t)groups * kWaves;
+  const int nw = groups * kWaves;
   pl.nw = nw < pl.units ? nw : pl.units;
+  pl.base = pl.units / pl.nw;
+  pl.rem = pl.units % pl.nw;
+  auto start_of = [&](int w) { return w * pl.base + (w < pl.rem ? w : pl.rem); };
   // Workgroups sharing one tile: at most (kp - 1) / (shortest CU range) + 2.
-  int64_t minlen = pl.units;
-  for (int64_t c = 0; c * kWaves < pl.nw; ++c) {
-    const int64_t w0 = c * kWaves, w1 = (c + 1) * kWaves < pl.nw ? (c + 1) * kWaves : pl.nw;
-    const int64_t len = w1 * pl.units / pl.nw - w0 * pl.units / pl.nw;
+  int minlen = pl.units;
+  for (int c = 0; c * kWaves < pl.nw; ++c) {
+    const int w0 = c * kWaves, w1 = (c + 1) * kWaves < pl.nw ? (c + 1) * kWaves : pl.nw;
+    const int len = start_of(w1) - start_of(w0);
     if (len < minlen) minlen = len;
   }
   pl.maxc = (int)((pl.kp - 1) / minlen) + 2;
