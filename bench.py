@@ -81,7 +81,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident codes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

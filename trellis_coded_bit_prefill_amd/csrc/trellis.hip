@@ -38,12 +38,12 @@ namespace trellis {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 12;                 // waves per prefill workgroup (3 per SIMD)
+constexpr int kWaves = 16;                 // waves per prefill workgroup (4 per SIMD)
 constexpr int kWgThreads = kWave * kWaves;
 constexpr int kTableBytes = 4096 * 4;      // window -> float value
 constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
-constexpr int kStageRegs = 12;             // x-staging vectors (16 B) per thread
+constexpr int kStageRegs = 9;              // x-staging vectors (16 B) per thread
 static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - kTableBytes, "x staging must cover the largest panel");
 
 // ---------------------------------------------------------------------------
@@ -93,22 +93,56 @@ struct Plan {
   int32_t x_stride;  // bytes per staged x row
   int32_t lds_bytes;
   int32_t units;     // tiles * kp (per panel), < 2^28
-  int32_t nw;        // active waves per panel: min(groups * waves, units)
-  int32_t base;      // units / nw: every active wave gets base or base + 1 units
-  int32_t rem;       // units % nw: the first rem waves get base + 1
+  int32_t cq;        // units / groups: every workgroup gets cq or cq + 1 units
+  int32_t cr;        // units % groups: the first cr workgroups get cq + 1
   uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
 };
 
-// First unit of active wave w: waves 0..rem-1 hold base + 1 units, the rest
-// base units, in order.
-__device__ __forceinline__ int range_start(int w, const Plan &pl) {
-  return w * pl.base + (w < pl.rem ? w : pl.rem);
+// Split of a workgroup's contiguous units [u0, u0 + len) into s <= 16
+// pieces, one per wave. Wave slot w decodes the piece at position
+// w / 2 when w is even and s - 1 - w / 2 when w is odd: the lowest slots --
+// which a SIMD serves first -- take both ends of the range, where the tiles
+// shared with other workgroups lie. Slots 0 .. r-1 (r = len % s) get one unit
+// more than the others; consecutive slots sit on different SIMDs, so every
+// SIMD's load is within one unit of the others'. In position order the
+// lengths are base + 1 for [0, ce), base for [ce, s - h) and base + 1 for
+// [s - h, s), with ce = ceil(r / 2) and h = floor(r / 2).
+struct CuSplit {
+  int u0, len, s, base, ce, h;
+};
+
+__device__ __forceinline__ CuSplit cu_split(int c, const Plan &pl) {
+  CuSplit q;
+  q.u0 = c * pl.cq + (c < pl.cr ? c : pl.cr);
+  q.len = pl.cq + (c < pl.cr ? 1 : 0);
+  q.s = q.len < kWaves ? q.len : kWaves;
+  q.base = q.s == kWaves ? q.len / kWaves : (int)((uint32_t)q.len / (uint32_t)q.s);
+  const int r = q.len - q.base * q.s;
+  q.ce = (r + 1) >> 1;
+  q.h = r >> 1;
+  return q;
 }
 
-// The active wave whose range holds unit u.
-__device__ __forceinline__ int owner_of(int u, const Plan &pl) {
-  const int cut = pl.rem * (pl.base + 1);
-  return u < cut ? u / (pl.base + 1) : pl.rem + (u - cut) / pl.base;
+// First unit of the piece at position p (0 <= p <= s).
+__device__ __forceinline__ int piece_start(const CuSplit &q, int p) {
+  const int tail = p - (q.s - q.h);
+  return q.u0 + p * q.base + (p < q.ce ? p : q.ce) + (tail > 0 ? tail : 0);
+}
+
+// Global index (workgroup * 16 + position) of the piece holding unit u;
+// consecutive pieces in unit order have consecutive indices.
+__device__ __forceinline__ int piece_of(int u, const Plan &pl) {
+  const int cut = pl.cr * (pl.cq + 1);
+  const int c = u < cut ? (int)((uint32_t)u / (uint32_t)(pl.cq + 1))
+                        : pl.cr + (int)((uint32_t)(u - cut) / (uint32_t)pl.cq);
+  const CuSplit q = cu_split(c, pl);
+  const int o = u - q.u0;
+  const int x1 = q.ce * (q.base + 1), x2 = x1 + (q.s - q.h - q.ce) * q.base;
+  int p;
+  if (o < x1) p = (int)((uint32_t)o / (uint32_t)(q.base + 1));
+  else if (o < x2) p = q.ce + (int)((uint32_t)(o - x1) / (uint32_t)q.base);
+  else p = q.s - q.h + (int)((uint32_t)(o - x2) / (uint32_t)(q.base + 1));
+  return c * kWaves + p;
 }
 
 // Lane (j, g) of a wave: j = row of the 16-row tile (B column) and x row (A
@@ -266,45 +300,69 @@ __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned ch
   (unit_group<BITS, MASK, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
+// Rows 4g .. 4g+3 of output column `row` (M <= 16 and N <= 2^22, so every
+// element offset fits in 32 bits).
 __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
   if (row >= n) return;
+  const uint32_t off = (uint32_t)(4 * g) * (uint32_t)n + (uint32_t)row;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = 4 * g + e;
-    if (i < m) out[(int64_t)i * n + row] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-  }
+  for (int e = 0; e < 4; ++e)
+    if (4 * g + e < m) out[off + (uint32_t)(e * n)] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
 }
 
-// Cross-CU completion of a tile whose units are split between workgroups.
-// The CU's partial is written with agent-scope relaxed atomic stores
-// (coherent across the per-XCD L2s) and every lane's stores are complete
-// (s_waitcnt vmcnt(0)) before lane 0 bumps the tile counter; the last
-// arriving contributor -- whose loads are issued only after its counter
-// update returned -- adds all partials in slot order (fixed, so the result
-// does not depend on arrival order), stores bf16 and resets the counter.
-// No cache-wide fence (L2 writeback/invalidate) is needed.
-__device__ __forceinline__ void finish_shared_tile(const Plan &pl, int tile, int panel, int slot_idx, int contrib,
-                                                   f32x4 acc, float *__restrict__ ws,
-                                                   uint32_t *__restrict__ counters, uint16_t *__restrict__ out,
-                                                   int lane) {
+// Partials of tiles shared with other workgroups go through the workspace:
+// slot [tile][panel][contributor] holds one 16x16 fp32 partial, lane-major.
+__device__ __forceinline__ float *partial_slot(const Plan &pl, float *ws, int tile, int panel, int idx, int lane) {
+  return ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + idx) * 256 + 4 * lane;
+}
+
+// Stores a lane's four partial sums without making the wave wait for them:
+// written as inline assembly, the stores are not tracked by the compiler's
+// memory-counter waits, so the next code-word loads are not held up behind
+// their acknowledgement. A later wait for a load still covers that load
+// (loads complete in order among themselves); an explicit s_waitcnt
+// vmcnt(0) after the main loop covers the stores. sc1: coherent across the
+// per-XCD L2s (agent scope). Four dword stores: no store-data hazard.
+__device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
+  asm volatile(
+      "global_store_dword %0, %1, off sc1\n\t"
+      "global_store_dword %0, %2, off offset:4 sc1\n\t"
+      "global_store_dword %0, %3, off offset:8 sc1\n\t"
+      "global_store_dword %0, %4, off offset:12 sc1"
+      :
+      : "v"(slot), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
+
+// Sum of a tile's staged partials, panel-major then contributor order. The
+// loads are issued in batches of sixteen slots before any of them is used,
+// so a batch costs one round trip to the coherent level rather than sixteen.
+__device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int tile, int contrib, int lane) {
+  constexpr int kBatch = 16;
   const int total = contrib * pl.panels;
-  float *slot = ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + slot_idx) * 256 + 4 * lane;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) __hip_atomic_store(slot + e, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old != (uint32_t)(total - 1)) return;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int pp = 0; pp < pl.panels; ++pp)
-    for (int cc = 0; cc < contrib; ++cc) {
-      float *src = ws + (((int64_t)tile * pl.panels + pp) * pl.maxc + cc) * 256 + 4 * lane;
+  int pp = 0, cc = 0;  // slot of the next load
+  for (int b0 = 0; b0 < total; b0 += kBatch) {
+    float v[kBatch][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum[e] += __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kBatch; ++i) {
+      // past the end: reload the last slot (valid memory, never added)
+      const float *src = partial_slot(pl, ws, tile, pp, cc, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[i][e] = __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b0 + i + 1 < total && ++cc == contrib) {
+        cc = 0;
+        ++pp;
+      }
     }
-  store_tile(out, sum, pl.m, pl.n, tile * 16 + (lane & 15), lane >> 4);
-  if (lane == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (b0 + i < total)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += v[i][e];
+  }
+  return sum;
 }
 
 template <int BITS, int MASK>
@@ -321,7 +379,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
   unsigned char *const xl = lds;
   constexpr int wpb = 8 * BITS;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane & 15, g = lane >> 4;
   const int panel = blockIdx.x % pl.panels;
   const int group = blockIdx.x / pl.panels;
@@ -329,13 +388,18 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   const int64_t kbase = (int64_t)panel * panel_k;
   const int64_t row_words = (int64_t)(pl.k >> 8) * wpb;
 
-  // Every active wave gets a non-empty range because nw <= units; waves
-  // beyond nw (tiny problems only) have nothing to do.
-  const int nw = pl.nw;
-  const int wave_id = group * kWaves + wave;
-  const bool active = wave_id < nw;
-  const int u0 = active ? range_start(wave_id, pl) : 0;
-  const int u1 = active ? range_start(wave_id + 1, pl) : 0;
+  // This workgroup's units [cu_u0, cu_u1) and this wave's piece of them.
+  const CuSplit q = cu_split(group, pl);
+  const int cu_u0 = q.u0, cu_u1 = q.u0 + q.len;
+  const int nseg = q.s;
+  const bool active = wave < q.s;
+  const int seg = (wave & 1) ? q.s - 1 - (wave >> 1) : (wave >> 1);  // position of the piece
+  const int u0 = active ? piece_start(q, seg) : 0;
+  const int u1 = active ? piece_start(q, seg + 1) : 0;
+  const int piece = group * kWaves + seg;
+  // A tile is "cross" when some of its units (of any panel) belong to another
+  // workgroup; its partials are combined through the workspace.
+  auto cross = [&](int t) { return pl.panels > 1 || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1; };
 
   // Rows past N (last tile only) read row 0's words and get scale 0, so
   // their weights are zero and their outputs are never stored.
@@ -351,10 +415,36 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   };
   auto scale_of = [&](int t, uint32_t bits) { return t * 16 + j < pl.n ? bf16_bits_to_f32((uint16_t)bits) : 0.f; };
 
-  // Prologue. x[:, panel] (M rows and an all-zero row M) is loaded and
-  // stored to LDS first, while the window -> value table is built; only then
-  // are code words requested, so the x loads do not queue behind every
-  // wave's burst of code-stream requests.
+  // Code words (and the row scale) of each unit live in one of two register
+  // slots: the unit being decoded and the next one in flight. The loop below
+  // is unrolled by two so the slots alternate without copying registers that
+  // still have loads pending.
+  struct Slot {
+    LaneWords<BITS> w;
+    uint32_t scb;  // raw bf16 scale bits
+  };
+  Slot S0, S1;
+  int tile = (int)((uint32_t)u0 / (uint32_t)pl.kp);
+  int b = u0 - tile * pl.kp;
+  int pt = tile, pb = b, pu = u0;  // next unit to request
+  auto advance = [&](int &t, int &bb) {
+    if (++bb == pl.kp) {
+      bb = 0;
+      ++t;
+    }
+  };
+  // Requests are unconditional (straight-line code keeps the compiler's
+  // memory-counter waits exact); once past the range they repeat its last
+  // unit, which is cache-resident and never decoded again.
+  auto request = [&](Slot &S) {
+    load_words<BITS>(unit_words(pt, pb), g, S.w);
+    S.scb = tile_scale_bits(pt);
+    if (++pu < u1) advance(pt, pb);
+  };
+  // Prologue. x[:, panel] (M rows and an all-zero row M) is requested
+  // first, then the first unit's code words (memory-counter waits are in
+  // issue order, so x can be stored to LDS without waiting for the codes);
+  // the window -> value table is built while both are in flight.
   const int vecs = panel_k / 8;
   const int xtotal = (pl.m + 1) * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
   {
@@ -368,6 +458,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         if (i < pl.m) xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
       }
     }
+    request(S0);
     for (int e = tid; e < 4096; e += kWgThreads) s_table[e] = trellis_value(code_of((uint32_t)e));
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
@@ -379,50 +470,29 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     }
   }
 
-  // Code words (and the row scale) of each unit live in one of three
-  // register slots: the unit being decoded and the next two in flight. The
-  // loop below is unrolled by three so the slots rotate without copying
-  // registers that still have loads pending.
-  struct Slot {
-    LaneWords<BITS> w;
-    uint32_t scb;  // raw bf16 scale bits
-  };
-  Slot S0, S1, S2;
-  int tile = (int)(u0 / pl.kp);
-  int b = u0 - tile * pl.kp;
-  int pt = tile, pb = b;  // next unit to request
-  auto advance = [&](int &t, int &bb) {
-    if (++bb == pl.kp) {
-      bb = 0;
-      ++t;
-    }
-  };
-  auto request = [&](Slot &S) {
-    load_words<BITS>(unit_words(pt, pb), g, S.w);
-    S.scb = tile_scale_bits(pt);
-    advance(pt, pb);
-  };
-  // Requests are unconditional (straight-line code keeps the compiler's
-  // memory-counter waits exact); past the end of the range they read valid,
-  // cache-resident words that are never decoded.
-  request(S0);
-  request(S1);
   __syncthreads();
 
   const unsigned char *xa = xl + (j < pl.m ? j : pl.m) * pl.x_stride + (192 - 64 * g) * 2;
 
-  // Tiles of this wave: the first may be shared with earlier waves and the
-  // last with later ones (both kept as partials until the end); complete
-  // tiles are stored as soon as they are done.
-  const int tf = (int)(u0 / pl.kp);
+  // Tiles of this wave's range: a cross tile's partial is staged in the
+  // workspace as soon as its units here are done (its counter is bumped after
+  // the loop); a tile whose units (of this panel) all lie in the range is
+  // stored; otherwise the first and last tile of the range may be shared with
+  // neighbouring pieces of this workgroup and are kept as partials for the
+  // combine below.
+  const int tf = tile;
+  int tl = tile;  // the range's last tile
   f32x4 part_f = {0.f, 0.f, 0.f, 0.f}, part_l = {0.f, 0.f, 0.f, 0.f};
-  // A tile whose units (of this panel) all lie in this wave: final when x
-  // has one panel; otherwise this wave is the panel's only contributor.
-  auto complete_tile = [&](int t, f32x4 v) {
-    if (pl.panels == 1) store_tile(out, v, pl.m, pl.n, t * 16 + j, g);
-    else finish_shared_tile(pl, t, panel, 0, 1, v, ws, counters, out, lane);
+  auto stage = [&](int t, f32x4 v) {
+    stage_partial(partial_slot(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane), v);
   };
-  if (u0 < u1) {
+  // A tile finished inside the loop is never the range's last tile.
+  auto tile_done = [&](int t, f32x4 v) {
+    if (cross(t)) stage(t, v);
+    else if (t == tf && u0 > t * pl.kp) part_f = v;
+    else store_tile(out, v, pl.m, pl.n, t * 16 + j, g);
+  };
+  if (active) {
     int cur = tile;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float s = scale_of(tile, S0.scb), q, kq;
@@ -430,12 +500,10 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     bool table_only = !__all(alu_scale_ok(s));
     const uint32_t mask3ffc = 0x3FFCu;
     int u = u0;
-    // Decode unit u from slot C while unit u + 2 is requested into slot N.
+    // Decode unit u from slot C while unit u + 1 is requested into slot N.
     auto step = [&](Slot &C, Slot &N) {
       if (tile != cur) {
-        // tile `cur` is done; only the range's first tile can be shared here
-        if (cur == tf && u0 > tf * pl.kp) part_f = acc;
-        else complete_tile(cur, acc);
+        tile_done(cur, acc);
         cur = tile;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
         s = scale_of(tile, C.scb);
@@ -452,75 +520,97 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       ++u;
     };
     for (;;) {
-      step(S0, S2);
+      step(S0, S1);
       if (u == u1) break;
       step(S1, S0);
       if (u == u1) break;
-      step(S2, S1);
-      if (u == u1) break;
     }
-    // the range's last tile
-    if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) complete_tile(cur, acc);
+    tl = cur;
+    if (cross(cur)) stage(cur, acc);
+    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(out, acc, pl.m, pl.n, cur * 16 + j, g);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
 
-  // ---- Combine shared tiles: within the CU through LDS, across CUs through
-  // the workspace. Wave w holds a partial of its first tile when its range
-  // does not cover that whole tile, and a partial of its last tile (when
-  // different) when its range ends inside it.
+  // ---- Publish the cross tiles of the range: once the staged partials are
+  // complete, bump each tile's counter (one lane per tile); the contributor
+  // that arrives last adds all partials in a fixed order (panel, then piece),
+  // so the result does not depend on arrival order, stores bf16 and resets
+  // the counter. Its loads are issued only after its counter update
+  // returned, and every other contributor's stores completed before its own
+  // update, so no cache-wide fence is needed.
+  if (active) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int t0 = tf; t0 <= tl; t0 += kWave) {
+      const int t = t0 + lane;
+      const bool mine = t <= tl && cross(t);
+      int contrib = 0;
+      uint32_t old = 0;
+      if (mine) {
+        contrib = piece_of((t + 1) * pl.kp - 1, pl) - piece_of(t * pl.kp, pl) + 1;
+        old = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      uint64_t last = __ballot(mine && old == (uint32_t)(contrib * pl.panels - 1));
+      while (last) {
+        const int i = __builtin_ctzll(last);
+        last &= last - 1;
+        const int T = t0 + i;
+        const int c = __shfl(contrib, i);
+        store_tile(out, sum_partials(pl, ws, T, c, lane), pl.m, pl.n, T * 16 + j, g);
+        if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
+  // ---- Combine the CU's own shared tiles through LDS. Segment s of the CU
+  // holds a partial of its first tile when its range does not cover that
+  // whole tile, and a partial of its last tile (when different) when its
+  // range ends inside it; cross tiles went through the workspace.
   __syncthreads();  // all waves are done reading x; its LDS holds the partials now
-  f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [wave][first, last][lane]
-  slots[(wave * 2 + 0) * kWave + lane] = part_f;
-  slots[(wave * 2 + 1) * kWave + lane] = part_l;
+  f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [segment][first, last][lane]
+  if (active) {
+    slots[(seg * 2 + 0) * kWave + lane] = part_f;
+    slots[(seg * 2 + 1) * kWave + lane] = part_l;
+  }
   __syncthreads();
   if (!active) return;
-
-  const int cu_w0 = group * kWaves;                              // first wave of this CU
-  const int cu_w1 = cu_w0 + kWaves < nw ? cu_w0 + kWaves : nw;  // one past its last active wave
-  const int cu_u0 = range_start(cu_w0, pl), cu_u1 = range_start(cu_w1, pl);
-  // The wave leads each shared tile of its range that no earlier wave of the
-  // CU holds, and adds the CU's partials of it in wave order.
+  // The segment leads each non-cross tile of its range that is not complete
+  // in it and that no earlier segment of the CU holds, and adds the CU's
+  // partials of it in segment order.
   for (int which = 0; which < 2; ++which) {
     int T;
     if (which == 0) {
-      T = u0 / pl.kp;
-      if (u0 == T * pl.kp && u1 >= (T + 1) * pl.kp) continue;  // complete in this wave
-      if (wave_id > cu_w0 && u0 > T * pl.kp) continue;          // an earlier wave of the CU holds T
+      T = tf;
+      if (u0 == T * pl.kp && u1 >= (T + 1) * pl.kp) continue;  // complete here
+      if (u0 > T * pl.kp) continue;                             // an earlier segment holds T
     } else {
-      T = (u1 - 1) / pl.kp;
-      if (T == u0 / pl.kp || u1 == (T + 1) * pl.kp) continue;  // same as the first, or complete
+      T = tl;
+      if (T == tf || u1 == (T + 1) * pl.kp) continue;  // same as the first, or complete
     }
+    if (cross(T)) continue;
+    const int t0u = T * pl.kp, t1u = t0u + pl.kp;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int w = wave_id; w < cu_w1; ++w) {
-      const int a = range_start(w, pl), e = range_start(w + 1, pl);
+    for (int sidx = seg; sidx < nseg; ++sidx) {
+      const int a = piece_start(q, sidx), e = piece_start(q, sidx + 1);
       int which_slot;
-      if (a / pl.kp == T) which_slot = 0;
-      else if ((e - 1) / pl.kp == T) which_slot = 1;
+      if (a >= t0u) which_slot = 0;       // the segment starts inside T
+      else if (e > t0u) which_slot = 1;   // the leader, whose range ends inside T
       else break;
-      const f32x4 v = slots[((int)(w - cu_w0) * 2 + which_slot) * kWave + lane];
+      const f32x4 v = slots[(sidx * 2 + which_slot) * kWave + lane];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
-      if ((e - 1) / pl.kp != T) break;
+      if (e >= t1u) break;  // T ends in this segment
     }
-    const int t0u = T * pl.kp, t1u = t0u + pl.kp;
-    if (t0u >= cu_u0 && t1u <= cu_u1 && pl.panels == 1) {
-      store_tile(out, sum, pl.m, pl.n, (int)T * 16 + j, g);
-    } else {
-      // CUs of this panel holding units of T, and this CU's index among them.
-      const int c0 = owner_of(t0u, pl) / kWaves;
-      const int c1 = owner_of(t1u - 1, pl) / kWaves;
-      finish_shared_tile(pl, (int)T, panel, (int)(group - c0), (int)(c1 - c0 + 1), sum, ws, counters, out, lane);
-    }
+    store_tile(out, sum, pl.m, pl.n, T * 16 + j, g);
   }
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
 // use ALU arithmetic.
 template <int BITS> struct Mix;
-template <> struct Mix<2> { static constexpr int kMask = 0b00001111; };
-template <> struct Mix<3> { static constexpr int kMask = 0b01011011; };
-template <> struct Mix<4> { static constexpr int kMask = 0b00110111; };
+template <> struct Mix<2> { static constexpr int kMask = 0b11110000; };
+template <> struct Mix<3> { static constexpr int kMask = 0b01010101; };
+template <> struct Mix<4> { static constexpr int kMask = 0b00110011; };
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -569,21 +659,14 @@ Plan make_plan(int m, int n, int k, int cus) {
   int groups = cus / panels;
   if (groups < 1) groups = 1;
   pl.units = pl.tiles * pl.kp;  // <= 2^18 tiles * 2^10 blocks
+  // Every workgroup gets at least kWaves units unless there is only one.
   while (groups > 1 && groups * kWaves > pl.units) --groups;
   pl.groups = groups;
-  const int nw = groups * kWaves;
-  pl.nw = nw < pl.units ? nw : pl.units;
-  pl.base = pl.units / pl.nw;
-  pl.rem = pl.units % pl.nw;
-  auto start_of = [&](int w) { return w * pl.base + (w < pl.rem ? w : pl.rem); };
-  // Workgroups sharing one tile: at most (kp - 1) / (shortest CU range) + 2.
-  int minlen = pl.units;
-  for (int c = 0; c * kWaves < pl.nw; ++c) {
-    const int w0 = c * kWaves, w1 = (c + 1) * kWaves < pl.nw ? (c + 1) * kWaves : pl.nw;
-    const int len = start_of(w1) - start_of(w0);
-    if (len < minlen) minlen = len;
-  }
-  pl.maxc = (int)((pl.kp - 1) / minlen) + 2;
+  pl.cq = pl.units / groups;
+  pl.cr = pl.units % groups;
+  // Pieces sharing one tile (per panel): at most (kp - 1) / (shortest piece) + 2.
+  const int s_min = pl.cq < kWaves ? pl.cq : kWaves;
+  pl.maxc = (pl.kp - 1) / (pl.cq / s_min) + 2;
   // Dynamic LDS (x panel); the static table adds kTableBytes.
   const int need = (m + 1) * pl.x_stride;
   pl.lds_bytes = need + kTableBytes > kMinLds ? need : kMinLds - kTableBytes;
