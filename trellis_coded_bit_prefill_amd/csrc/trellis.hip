@@ -157,25 +157,31 @@ struct LaneWords {
   uint32_t d[2 * BITS + 1];
 };
 
+// Code words are read through a buffer resource whose base is the unit's
+// block in the tile's first row and whose size ends at the last valid row:
+// every lane's offset is then a per-lane constant (j * row bytes + its word
+// range), the unit's position is scalar, and the rows past N of the last
+// tile fall outside the range, which the hardware reads as zero.
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw-buffer descriptor word 3
+
 template <int BITS>
-__device__ __forceinline__ void load_words(const uint32_t *__restrict__ blk, int g, LaneWords<BITS> &L) {
-  constexpr int wpb = 8 * BITS;
-  const uint32_t *p = blk + 2 * BITS * g;
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t off_next,
+                                           LaneWords<BITS> &L) {
   if constexpr (BITS == 4) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(p);
-    const uint4 b = *reinterpret_cast<const uint4 *>(p + 4);
-    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = a.z; L.d[3] = a.w;
-    L.d[4] = b.x; L.d[5] = b.y; L.d[6] = b.z; L.d[7] = b.w;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+    L.d[0] = a[0]; L.d[1] = a[1]; L.d[2] = a[2]; L.d[3] = a[3];
+    L.d[4] = b[0]; L.d[5] = b[1]; L.d[6] = b[2]; L.d[7] = b[3];
   } else if constexpr (BITS == 3) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(p);
-    const uint2 b = *reinterpret_cast<const uint2 *>(p + 2);
-    const uint2 c = *reinterpret_cast<const uint2 *>(p + 4);
-    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = b.x; L.d[3] = b.y; L.d[4] = c.x; L.d[5] = c.y;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8, 0, 0);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, 0);
+    L.d[0] = a[0]; L.d[1] = a[1]; L.d[2] = b[0]; L.d[3] = b[1]; L.d[4] = c[0]; L.d[5] = c[1];
   } else {
-    const uint4 a = *reinterpret_cast<const uint4 *>(p);
-    L.d[0] = a.x; L.d[1] = a.y; L.d[2] = a.z; L.d[3] = a.w;
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    L.d[0] = a[0]; L.d[1] = a[1]; L.d[2] = a[2]; L.d[3] = a[3];
   }
-  L.d[2 * BITS] = blk[(2 * BITS * (g + 1)) % wpb];
+  L.d[2 * BITS] = __builtin_amdgcn_raw_buffer_load_b32(r, off_next, 0, 0);
 }
 
 __device__ __forceinline__ float lds_table(const unsigned char *table, uint32_t byte_addr) {
@@ -386,7 +392,6 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   const int group = blockIdx.x / pl.panels;
   const int panel_k = pl.kp * 256;
   const int64_t kbase = (int64_t)panel * panel_k;
-  const int64_t row_words = (int64_t)(pl.k >> 8) * wpb;
 
   // This workgroup's units [cu_u0, cu_u1) and this wave's piece of them.
   const CuSplit q = cu_split(group, pl);
@@ -401,19 +406,30 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // workgroup; its partials are combined through the workspace.
   auto cross = [&](int t) { return pl.panels > 1 || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1; };
 
-  // Rows past N (last tile only) read row 0's words and get scale 0, so
-  // their weights are zero and their outputs are never stored.
-  auto unit_words = [&](int t, int bb) {
-    const int row = t * 16 + j;
-    return codes + (int64_t)(row < pl.n ? row : 0) * row_words + ((int64_t)panel * pl.kp + bb) * wpb;
+  // Per-lane byte offsets of the code words inside a unit's buffer (see
+  // load_words) and of the row scale inside its tile's scale buffer.
+  const uint32_t row_bytes = (uint32_t)(pl.k >> 8) * wpb * 4;
+  const uint32_t lane_off = (uint32_t)j * row_bytes + (uint32_t)g * (8 * BITS);
+  const uint32_t lane_off_next = (uint32_t)j * row_bytes + (uint32_t)((2 * BITS * (g + 1)) % wpb) * 4;
+  const uint32_t lane_off_scale = (uint32_t)j * 2;
+  // Buffers of unit (t, bb) and of tile t's scales: rows past N are outside
+  // them, so their words and scales read as zero (zero weights, never stored).
+  auto unit_buffer = [&](int t, int bb) {
+    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
+    const uint32_t blk_off = (uint32_t)(panel * pl.kp + bb) * (wpb * 4);
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(codes) +
+                                (int64_t)t * 16 * row_bytes + blk_off;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(base), (short)0,
+                                             (int)((uint32_t)rows * row_bytes - blk_off), kRawBufferWord3);
   };
-  // Raw scale bits of this lane's row in tile t (row 0's for rows past N);
-  // converted only when the tile starts, so the load is not waited for early.
-  auto tile_scale_bits = [&](int t) -> uint32_t {
-    const int row = t * 16 + j;
-    return scales[row < pl.n ? row : 0];
+  auto scale_buffer = [&](int t) {
+    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales + (int64_t)t * 16), (short)0,
+                                             rows * 2, kRawBufferWord3);
   };
-  auto scale_of = [&](int t, uint32_t bits) { return t * 16 + j < pl.n ? bf16_bits_to_f32((uint16_t)bits) : 0.f; };
+  // Raw scale bits are converted only when the tile starts, so the load is
+  // not waited for early.
+  auto scale_of = [&](uint32_t bits) { return bf16_bits_to_f32((uint16_t)bits); };
 
   // Code words (and the row scale) of each unit live in one of two register
   // slots: the unit being decoded and the next one in flight. The loop below
@@ -437,8 +453,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // memory-counter waits exact); once past the range they repeat its last
   // unit, which is cache-resident and never decoded again.
   auto request = [&](Slot &S) {
-    load_words<BITS>(unit_words(pt, pb), g, S.w);
-    S.scb = tile_scale_bits(pt);
+    load_words<BITS>(unit_buffer(pt, pb), lane_off, lane_off_next, S.w);
+    S.scb = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(pt), lane_off_scale, 0, 0);
     if (++pu < u1) advance(pt, pb);
   };
   // Prologue. x[:, panel] (M rows and an all-zero row M) is requested
@@ -495,7 +511,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   if (active) {
     int cur = tile;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float s = scale_of(tile, S0.scb), q, kq;
+    float s = scale_of(S0.scb), q, kq;
     alu_row_constants(s, q, kq);
     bool table_only = !__all(alu_scale_ok(s));
     const uint32_t mask3ffc = 0x3FFCu;
@@ -506,7 +522,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         tile_done(cur, acc);
         cur = tile;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        s = scale_of(tile, C.scb);
+        s = scale_of(C.scb);
         alu_row_constants(s, q, kq);
         table_only = !__all(alu_scale_ok(s));
       }
