@@ -323,40 +323,42 @@ __device__ __forceinline__ float *partial_slot(const Plan &pl, float *ws, int ti
 }
 
 // Stores a lane's four partial sums without making the wave wait for them:
-// written as inline assembly, the stores are not tracked by the compiler's
+// written as inline assembly, the store is not tracked by the compiler's
 // memory-counter waits, so the next code-word loads are not held up behind
-// their acknowledgement. A later wait for a load still covers that load
-// (loads complete in order among themselves); an explicit s_waitcnt
-// vmcnt(0) after the main loop covers the stores. sc1: coherent across the
-// per-XCD L2s (agent scope). Four dword stores: no store-data hazard.
+// its acknowledgement. A later wait for a load still covers that load (loads
+// complete in order among themselves); the explicit s_waitcnt vmcnt(0) after
+// the main loop covers the store. sc1: written through to the level that is
+// coherent across the per-XCD L2s (agent scope). One 16-byte store per lane
+// keeps every write a whole cache line per wave; the s_nop covers the
+// store-data hazard of stores wider than 8 bytes.
 __device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
   asm volatile(
-      "global_store_dword %0, %1, off sc1\n\t"
-      "global_store_dword %0, %2, off offset:4 sc1\n\t"
-      "global_store_dword %0, %3, off offset:8 sc1\n\t"
-      "global_store_dword %0, %4, off offset:12 sc1"
+      "global_store_dwordx4 %0, %1, off sc1\n\t"
+      "s_nop 1"
       :
-      : "v"(slot), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "v"(slot), "v"(v)
       : "memory");
 }
 
 // Sum of a tile's staged partials, panel-major then contributor order. The
-// loads are issued in batches of sixteen slots before any of them is used,
-// so a batch costs one round trip to the coherent level rather than sixteen.
+// loads (16 bytes per lane, sc1: from the coherent level) are issued in
+// batches of sixteen slots before any of them is used, so a batch costs one
+// round trip rather than sixteen.
 __device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int tile, int contrib, int lane) {
   constexpr int kBatch = 16;
+  constexpr int kSc1 = 16;  // cache-policy bits of the loads
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      partial_slot(pl, ws, tile, 0, 0, 0), (short)0, pl.panels * pl.maxc * 1024, kRawBufferWord3);
   const int total = contrib * pl.panels;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   int pp = 0, cc = 0;  // slot of the next load
   for (int b0 = 0; b0 < total; b0 += kBatch) {
-    float v[kBatch][4];
+    f32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       // past the end: reload the last slot (valid memory, never added)
-      const float *src = partial_slot(pl, ws, tile, pp, cc, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[i][e] = __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t off = (uint32_t)(pp * pl.maxc + cc) * 1024 + (uint32_t)lane * 16;
+      v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
       if (b0 + i + 1 < total && ++cc == contrib) {
         cc = 0;
         ++pp;
