@@ -24,16 +24,18 @@ def from_dev_bf16(t) -> np.ndarray:
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def exhaustive_window_codes(rng: np.random.Generator, nrows: int, bits: int):
+def exhaustive_window_codes(rng: np.random.Generator, nrows: int, bits: int, shift: int = 0):
     """Code rows in which every 12-bit window value 0..4095 occurs.
 
     In each block, weights t = t0, t0 + s, t0 + 2s, ... (s = ceil(12/bits),
-    t0 the first weight whose window does not wrap) read disjoint bit spans,
-    so their windows can be written freely; the remaining bits are random.
+    t0 the first weight whose window does not wrap, plus `shift`) read
+    disjoint bit spans, so their windows can be written freely; the remaining
+    bits are random. `shift` moves the written windows to other weight
+    positions (for k = 2 all of t0 + s*i share one parity).
     Returns (codes [nrows, K*bits/32], K).
     """
     s = -(-12 // bits)
-    t0 = -(-(12 - bits) // bits)
+    t0 = -(-(12 - bits) // bits) + shift
     slots = list(range(t0, 256, s))
     nblocks = -(-4096 // len(slots))
     k = 256 * nblocks

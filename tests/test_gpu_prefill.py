@@ -133,22 +133,24 @@ def test_prefill_k_panels_with_whole_tiles_per_wave():
     assert_prefill_close(out[:, rows], y, a, "panels+whole tiles")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
-def test_prefill_weights_bit_exact_every_window_and_scale(bits):
+@pytest.mark.parametrize("bits,shift", [(2, 0), (2, 1), (3, 0), (4, 0)])
+def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift):
     # One-hot x rows pick single columns of W, so every output is one decoded
     # weight (sum of one exact product): prefill's in-kernel decode (both the
     # LDS-table and the ALU path) must give exactly the oracle's weights.
     # Rows hold all 4096 windows; scales cover the 257 reachable values, both
     # signs, zero, and magnitudes outside 2^-110..2^110 (table-only rows).
+    # For k = 2 the two shifts put the written windows at odd and at even
+    # weight positions: both halves of a pair-table entry.
     import torch
 
-    print(f"prefill one-hot exhaustive bits={bits}", flush=True)
-    rng = np.random.default_rng(600 + bits)
+    print(f"prefill one-hot exhaustive bits={bits} shift={shift}", flush=True)
+    rng = np.random.default_rng(600 + bits + 10 * shift)
     extra = [0x3F80, 0xBF80, 0xBC00, 0xBCA4, 0x0000, 0x8000, 0x0B00, 0x7300, 0x3FFF, 0xC07F,
              0x0600, 0x7900, 0x8600]
     scales = np.concatenate([np.arange(0x3BA4, 0x3CA5, dtype=np.uint16), np.array(extra, dtype=np.uint16)])
     scales = np.concatenate([scales, np.full((-scales.size) % 16, 0x3C00, dtype=np.uint16)])
-    codes, k = exhaustive_window_codes(rng, scales.size, bits)
+    codes, k = exhaustive_window_codes(rng, scales.size, bits, shift)
     w_ref = oracle.decode(codes, scales, k, bits)
     cd, sd = to_dev_codes(codes), to_dev_bf16(scales)
     m = 15

@@ -158,4 +158,52 @@ __device__ __forceinline__ void quad_x4(const uint32_t (&D)[N], uint32_t mask, u
   a[3] = and_hi16(hi, mask);
 }
 
+// ---- k = 2 pair table -------------------------------------------------------
+// For k = 2 the windows of weights idx and idx + 1 (idx even) overlap in 10
+// bits: the 14 stream bits from the lower window's start hold both. A
+// 16384-entry table indexed by those 14 bits gives both codes at once, as
+// two float16 values (every code in [-510, 510] is exact in float16): the
+// high half holds the code of the upper 12 bits (weight idx), the low half
+// that of the lower 12 bits (weight idx + 1).
+__device__ __forceinline__ uint32_t pair_entry(uint32_t p) {
+  const float hi = (float)code_of(p >> 2), lo = (float)code_of(p & 0xFFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// Table byte addresses (pair * 4) of the two 14-bit pair fields whose lowest
+// bits are at O0 and O0 + 16: one word holding stream bits [O0-2, O0+30) is
+// built, and each address is one mask of its low or high half.
+template <int O0, int N>
+__device__ __forceinline__ void pair_x4(const uint32_t (&D)[N], uint32_t mask, uint32_t (&a)[2]) {
+  constexpr int sh = O0 - 2;
+  uint32_t w;
+  if constexpr (sh < 0) {
+    static_assert(sh == -2, "unexpected pair offset");
+    w = D[0] << 2;
+  } else {
+    constexpr int wi = sh >> 5, r = sh & 31;
+    if constexpr (r == 0) {
+      w = D[wi];
+    } else {
+      static_assert(wi + 1 < N, "pair outside the lane's words");
+      w = __builtin_amdgcn_alignbit(D[wi + 1], D[wi], r);
+    }
+  }
+  a[0] = w & 0xFFFCu;
+  a[1] = and_hi16(w, mask);
+}
+
+// float32(code * q) from the low or high float16 half of a pair entry, one
+// fused multiply-add of mixed precision (the code converts exactly).
+__device__ __forceinline__ float mix_lo(uint32_t h2, float q) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(q));
+  return r;
+}
+__device__ __forceinline__ float mix_hi(uint32_t h2, float q) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(q));
+  return r;
+}
+
 }  // namespace trellis

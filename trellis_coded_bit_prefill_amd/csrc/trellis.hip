@@ -40,11 +40,14 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 16;                 // waves per prefill workgroup (4 per SIMD)
 constexpr int kWgThreads = kWave * kWaves;
-constexpr int kTableBytes = 4096 * 4;      // window -> float value
+// LDS decode table: window -> float value (4096 entries), or for k = 2
+// 14-bit pair -> two float16 codes (16384 entries).
+constexpr int table_bytes(bool pair) { return pair ? 16384 * 4 : 4096 * 4; }
 constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
 constexpr int kStageRegs = 9;              // x-staging vectors (16 B) per thread
-static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - kTableBytes, "x staging must cover the largest panel");
+constexpr int kCombineBytes = kWaves * 2 * kWave * 16;  // LDS partial tiles of the end-of-kernel combine
+static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(false), "x staging must cover the largest panel");
 
 // ---------------------------------------------------------------------------
 // trellis_decode: W[N, K] bf16. One thread per 8 consecutive weights of one
@@ -275,11 +278,73 @@ constexpr bool in_span() {
   else return false;
 }
 
-template <int BITS, int MASK, int U>
+// k = 2 with the pair table: groups (U, U + 1), U even, share four pair
+// fields per 8 weights each (16 bits apart: pair i of group U + 1 in the low
+// half of a shifted word, pair i of group U in its high half).
+template <int U, int N>
+__device__ __forceinline__ void pair_span(const uint32_t (&D)[N], const unsigned char *table, float q,
+                                          uint32_t mask, bf16x8 (&w)[2]) {
+  float f[2][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a[2];
+    switch (i) {
+      case 0: pair_x4<108 - 16 * U - 0>(D, mask, a); break;
+      case 1: pair_x4<108 - 16 * U - 4>(D, mask, a); break;
+      case 2: pair_x4<108 - 16 * U - 8>(D, mask, a); break;
+      default: pair_x4<108 - 16 * U - 12>(D, mask, a); break;
+    }
+    const uint32_t g1 = *reinterpret_cast<const uint32_t *>(table + a[0]);
+    const uint32_t g0 = *reinterpret_cast<const uint32_t *>(table + a[1]);
+    f[1][2 * i] = mix_hi(g1, q);
+    f[1][2 * i + 1] = mix_lo(g1, q);
+    f[0][2 * i] = mix_hi(g0, q);
+    f[0][2 * i + 1] = mix_lo(g0, q);
+  }
+#pragma unroll
+  for (int gidx = 0; gidx < 2; ++gidx)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[gidx][e] = (__bf16)f[gidx][e];
+}
+
+// The pages' arithmetic on the ALU (window, hash, byte sum, reciprocal
+// refinement, scale): the exact fallback of the pair-table kernel for rows
+// whose scale is outside the range where code * q is exact.
+template <int BITS, int U, int... S>
+__device__ __forceinline__ bf16x8 group_exact(const LaneWords<BITS> &L, float s, std::integer_sequence<int, S...>) {
+  const float f[8] = {(trellis_value(code_of(win12<(63 - 8 * U - S) * BITS>(L.d))) * s)...};
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
+  return w;
+}
+
+template <int BITS, int MASK, bool PAIR, bool EXACT, int U>
 __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsigned char *table,
                                            const unsigned char *xa, float s, float q, float k, uint32_t mask,
                                            f32x4 &acc) {
-  if constexpr (span_start<BITS, MASK, U>()) {
+  if constexpr (EXACT) {
+    const bf16x8 w = group_exact<BITS, U>(L, s, std::make_integer_sequence<int, 8>{});
+    const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+  } else if constexpr (PAIR) {
+    static_assert(BITS == 2, "the pair table is for k = 2");
+    constexpr bool span = ((MASK >> (U - U % 2)) & 3) == 3;
+    if constexpr (span && U % 2 == 0) {
+      bf16x8 w[2];
+      pair_span<U>(L.d, table, q, mask, w);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * (U + i));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w[i], acc, 0, 0, 0);
+      }
+    } else if constexpr (!span) {
+      static_assert(((MASK >> U) & 1) == 0, "pair-table groups come in aligned pairs");
+      const bf16x8 w = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
+      const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+    }
+  } else if constexpr (span_start<BITS, MASK, U>()) {
     constexpr int G = BITS == 4 ? 2 : 4;
     bf16x8 w[G];
     table_span<BITS, U>(L, table, s, mask, w);
@@ -299,15 +364,13 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
   }
 }
 
-template <int BITS, int MASK, int... U>
+template <int BITS, int MASK, bool PAIR, bool EXACT, int... U>
 __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned char *table, const unsigned char *xa,
                                      float s, float q, float k, uint32_t mask, f32x4 &acc,
                                      std::integer_sequence<int, U...>) {
-  (unit_group<BITS, MASK, U>(L, table, xa, s, q, k, mask, acc), ...);
+  (unit_group<BITS, MASK, PAIR, EXACT, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
-// Rows 4g .. 4g+3 of output column `row` (M <= 16 and N <= 2^22, so every
-// element offset fits in 32 bits).
 __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
   if (row >= n) return;
   const uint32_t off = (uint32_t)(4 * g) * (uint32_t)n + (uint32_t)row;
@@ -373,7 +436,7 @@ __device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int til
   return sum;
 }
 
-template <int BITS, int MASK>
+template <int BITS, int MASK, bool PAIR>
 __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__restrict__ x,
                                                              const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
@@ -382,7 +445,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
   // After the main loop the x region is reused for the waves' partial tiles.
-  __shared__ __attribute__((aligned(16))) float s_table[4096];
+  __shared__ __attribute__((aligned(16))) uint32_t s_table[table_bytes(PAIR) / 4];
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
   unsigned char *const xl = lds;
@@ -477,7 +540,12 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       }
     }
     request(S0);
-    for (int e = tid; e < 4096; e += kWgThreads) s_table[e] = trellis_value(code_of((uint32_t)e));
+    if constexpr (PAIR) {
+      for (int e = tid; e < 16384; e += kWgThreads) s_table[e] = pair_entry((uint32_t)e);
+    } else {
+      for (int e = tid; e < 4096; e += kWgThreads)
+        s_table[e] = __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)e)));
+    }
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
       const int idx = r * kWgThreads + tid;
@@ -516,7 +584,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     float s = scale_of(S0.scb), q, kq;
     alu_row_constants(s, q, kq);
     bool table_only = !__all(alu_scale_ok(s));
-    const uint32_t mask3ffc = 0x3FFCu;
+    const uint32_t mask_addr = PAIR ? 0xFFFCu : 0x3FFCu;  // table byte-address mask (SDWA operand)
     int u = u0;
     // Decode unit u from slot C while unit u + 1 is requested into slot N.
     auto step = [&](Slot &C, Slot &N) {
@@ -530,10 +598,12 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       }
       request(N);
       const unsigned char *xb = xa + b * 512;
+      // Rows whose scale is outside the exact range of code * q: the value
+      // table (or, with the pair table, the ALU chain) for every group.
       if (table_only)
-        unit<BITS, 0xFF>(C.w, table, xb, s, q, kq, mask3ffc, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, 0xFF, false, PAIR>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
       else
-        unit<BITS, MASK>(C.w, table, xb, s, q, kq, mask3ffc, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, MASK, PAIR, false>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
       advance(tile, b);
       ++u;
     };
@@ -624,9 +694,10 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
-// use ALU arithmetic.
-template <int BITS> struct Mix;
+// use ALU arithmetic. PAIR: k = 2 with the pair table.
+template <int BITS, bool PAIR = false> struct Mix;
 template <> struct Mix<2> { static constexpr int kMask = 0b11110000; };
+template <> struct Mix<2, true> { static constexpr int kMask = 0b11111111; };
 template <> struct Mix<3> { static constexpr int kMask = 0b01010101; };
 template <> struct Mix<4> { static constexpr int kMask = 0b00110011; };
 
@@ -649,7 +720,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 void clear_last_error() { (void)hipGetLastError(); }
 trellis_status launch_status() { return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_E_HIP; }
 
-Plan make_plan(int m, int n, int k, int cus) {
+Plan make_plan(int m, int n, int k, int cus, int table) {
   Plan pl{};
   pl.m = m;
   pl.n = n;
@@ -660,7 +731,7 @@ Plan make_plan(int m, int n, int k, int cus) {
   for (int p = 1; p <= kb; ++p) {
     if (kb % p) continue;
     const int stride = (kb / p) * 512 + 16;
-    if (kTableBytes + (m + 1) * stride <= kMaxLds) {
+    if (table + (m + 1) * stride <= kMaxLds) {
       panels = p;
       break;
     }
@@ -685,15 +756,20 @@ Plan make_plan(int m, int n, int k, int cus) {
   // Pieces sharing one tile (per panel): at most (kp - 1) / (shortest piece) + 2.
   const int s_min = pl.cq < kWaves ? pl.cq : kWaves;
   pl.maxc = (pl.kp - 1) / (pl.cq / s_min) + 2;
-  // Dynamic LDS (x panel); the static table adds kTableBytes.
-  const int need = (m + 1) * pl.x_stride;
-  pl.lds_bytes = need + kTableBytes > kMinLds ? need : kMinLds - kTableBytes;
+  // Dynamic LDS: the x panel, later reused for the pieces' partial tiles
+  // (two 16x16 fp32 tiles per wave); the static table adds `table` bytes.
+  int need = (m + 1) * pl.x_stride;
+  if (need < kCombineBytes) need = kCombineBytes;
+  pl.lds_bytes = need + table > kMinLds ? need : kMinLds - table;
   return pl;
 }
 
+// Prefill kernels: k = 2 (value table), 3, 4, and k = 2 with the pair table.
+enum Variant { kK2 = 0, kK3 = 1, kK4 = 2, kK2Pair = 3, kVariants = 4 };
+
 struct DeviceState {
   int cus = 0;
-  bool lds_attr_set[3] = {false, false, false};
+  bool lds_attr_set[kVariants] = {false, false, false, false};
 };
 
 struct Workspace {
@@ -707,12 +783,16 @@ std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-template <int BITS>
-const void *prefill_fn() {
-  return reinterpret_cast<const void *>(&prefill_kernel<BITS, Mix<BITS>::kMask>);
+const void *prefill_fn(Variant v) {
+  switch (v) {
+    case kK2: return reinterpret_cast<const void *>(&prefill_kernel<2, Mix<2>::kMask, false>);
+    case kK3: return reinterpret_cast<const void *>(&prefill_kernel<3, Mix<3>::kMask, false>);
+    case kK4: return reinterpret_cast<const void *>(&prefill_kernel<4, Mix<4>::kMask, false>);
+    default: return reinterpret_cast<const void *>(&prefill_kernel<2, Mix<2, true>::kMask, true>);
+  }
 }
 
-trellis_status device_state(DeviceState *&st, int bits) {
+trellis_status device_state(DeviceState *&st, Variant v) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
   DeviceState &d = g_dev[dev];
@@ -720,11 +800,11 @@ trellis_status device_state(DeviceState *&st, int bits) {
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || d.cus <= 0)
       return TRELLIS_E_HIP;
   }
-  if (!d.lds_attr_set[bits - 2]) {
-    const void *fn = bits == 2 ? prefill_fn<2>() : bits == 3 ? prefill_fn<3>() : prefill_fn<4>();
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - kTableBytes) != hipSuccess)
+  if (!d.lds_attr_set[v]) {
+    if (hipFuncSetAttribute(prefill_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLds - table_bytes(v == kK2Pair)) != hipSuccess)
       return TRELLIS_E_HIP;
-    d.lds_attr_set[bits - 2] = true;
+    d.lds_attr_set[v] = true;
   }
   st = &d;
   return TRELLIS_OK;
@@ -804,27 +884,48 @@ trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t
     return TRELLIS_E_ALIGN;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   std::lock_guard<std::mutex> lock(g_mu);
+  int cus = 0;
+  {
+    DeviceState *st0 = nullptr;
+    const trellis_status rc0 = device_state(st0, g.bits == 3 ? kK3 : g.bits == 4 ? kK4 : kK2);
+    if (rc0 != TRELLIS_OK) return rc0;
+    cus = st0->cus;
+  }
+  // k = 2 uses the pair table unless its larger footprint would split x
+  // into more K panels than the value table does.
+  Variant v = g.bits == 3 ? kK3 : g.bits == 4 ? kK4 : kK2;
+  Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(false));
+  if (v == kK2) {
+    const Plan pp = make_plan(m, g.n, g.k, cus, table_bytes(true));
+    if (pp.panels == pl.panels) {
+      pl = pp;
+      v = kK2Pair;
+    }
+  }
   DeviceState *st = nullptr;
-  trellis_status rc = device_state(st, g.bits);
+  trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
-  const Plan pl = make_plan(m, g.n, g.k, st->cus);
   Workspace *w = nullptr;
   rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256, (size_t)pl.tiles, w);
   if (rc != TRELLIS_OK) return rc;
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
-  switch (g.bits) {
-    case 2:
-      hipLaunchKernelGGL((prefill_kernel<2, Mix<2>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
-                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+  switch (v) {
+    case kK2:
+      hipLaunchKernelGGL((prefill_kernel<2, Mix<2>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
+                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
       break;
-    case 3:
-      hipLaunchKernelGGL((prefill_kernel<3, Mix<3>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
-                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+    case kK3:
+      hipLaunchKernelGGL((prefill_kernel<3, Mix<3>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
+                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
+      break;
+    case kK4:
+      hipLaunchKernelGGL((prefill_kernel<4, Mix<4>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
+                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
       break;
     default:
-      hipLaunchKernelGGL((prefill_kernel<4, Mix<4>::kMask>), grid, block, pl.lds_bytes, stream, x_bf16, codes,
-                         scales_bf16, out_bf16, w->ws, w->counters, pl);
+      hipLaunchKernelGGL((prefill_kernel<2, Mix<2, true>::kMask, true>), grid, block, pl.lds_bytes, stream, x_bf16,
+                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
       break;
   }
   return launch_status();
