@@ -8,6 +8,9 @@ in HBM. Inputs rotate over enough independent sets that the code streams do
 not fit in the 256 MB Infinity Cache ("cold"), so every step reads its codes
 from HBM.
 
+The GPU raises its clocks only after some milliseconds of sustained work, so
+the default warm-up is 2000 launches (about 40 ms) before the timed region.
+
 Prints one JSON line:
   value = packed-code GB/s = (N*K*k/8 + 2*M*K + 2*M*N) bytes / step time
   roofline = the prefill kernel's algorithmic bytes / its average duration
@@ -81,8 +84,8 @@ def cpu_baseline(shape, passes: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--warm", action="store_true", help="one input set (cache-resident codes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

@@ -40,10 +40,17 @@
  *   NULL. The page's fixed K = 5120 is generalised to any multiple of 256.
  *
  * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
- * the default stream) and returns without waiting. No call allocates,
- * frees or synchronises, and none keeps any state between calls. Calls on
- * different streams are independent. Errors are returned, never thrown;
- * a validation error leaves every output untouched.
+ * the default stream) and returns without waiting. trellis_decode keeps no
+ * state. trellis_prefill sums tiles that are split across workgroups
+ * through a workspace (float32 partial tiles and per-tile counters) owned by
+ * the library, one per (device, stream): it is allocated with hipMalloc on
+ * the first call that needs it, grown (never shrunk or freed) when a later
+ * call on that stream needs more, and kept until the process exits; the
+ * kernel leaves its counters at zero for the next call. Calls on different
+ * streams therefore never share a workspace; calls on one stream are
+ * ordered by the stream. Host-side state is guarded by a mutex, so calls
+ * may come from several threads. Errors are returned, never thrown; a
+ * validation error leaves every output untouched.
  */
 #ifndef TRELLIS_H
 #define TRELLIS_H

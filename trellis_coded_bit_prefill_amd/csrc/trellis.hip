@@ -606,6 +606,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         unit<BITS, MASK, PAIR, false>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
       advance(tile, b);
       ++u;
+      // A SIMD issues from its highest-priority ready wave, oldest first
+      // among equals; ranking waves by the units they have left lets the
+      // younger waves catch up instead of running alone at the end.
+      const int rem = u1 - u;
+      if (rem >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (rem == 2) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(1);
     };
     for (;;) {
       step(S0, S1);
