@@ -150,9 +150,12 @@ def main():
     ptrs = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr()) for s in sets]
     lib = tp.load_library()
 
+    # M = 1..4 is the matvec entry point (same kernel and decode).
+    entry = lib.trellis_matvec if shape.m < tp.MIN_M else lib.trellis_prefill
+
     def step(i):
         xp, cp, sp, op = ptrs[i % nsets]
-        rc = lib.trellis_prefill(xp, shape.m, cp, sp, g, op, handle)
+        rc = entry(xp, shape.m, cp, sp, g, op, handle)
         if rc != 0:
             raise RuntimeError(tp.status_string(rc))
 

@@ -35,7 +35,7 @@
  *   K % 256 == 0, 256 <= K <= TRELLIS_MAX_K;
  *   N % 4 == 0, 4 <= N <= TRELLIS_MAX_N;
  *   5 <= M <= 15 for trellis_prefill (the narrow-batch regime of the page's
- *   eligibility predicate);
+ *   eligibility predicate), 1 <= M <= 4 for trellis_matvec;
  *   x, codes, out and w 16-byte aligned; scales 2-byte aligned; no pointer
  *   NULL. The page's fixed K = 5120 is generalised to any multiple of 256.
  *
@@ -65,6 +65,7 @@ extern "C" {
 #define TRELLIS_L 12
 #define TRELLIS_MIN_M 5
 #define TRELLIS_MAX_M 15
+#define TRELLIS_MATVEC_MAX_M 4
 #define TRELLIS_MAX_K (1 << 18)
 #define TRELLIS_MAX_N (1 << 22)
 
@@ -82,7 +83,7 @@ typedef struct trellis_geom {
 typedef enum trellis_status {
     TRELLIS_OK = 0,
     TRELLIS_E_GEOMETRY = -1, /* t, l, bits, n or k outside the accepted domain */
-    TRELLIS_E_M = -2,        /* m outside [5, 15] */
+    TRELLIS_E_M = -2,        /* m outside [5, 15] (prefill) or [1, 4] (matvec) */
     TRELLIS_E_NULL = -3,     /* a required pointer is NULL */
     TRELLIS_E_ALIGN = -4,    /* a pointer is not aligned as documented */
     TRELLIS_E_HIP = -5       /* the HIP runtime reported a launch error */
@@ -107,6 +108,20 @@ trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16
 trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m,
                                const uint32_t *codes, const uint16_t *scales_bf16,
                                trellis_geom g, uint16_t *out_bf16, void *hip_stream);
+
+/* The small-batch regime below the wide kernel's M = 5: 1 <= m <= 4 rows
+ * (decode tokens), same formats, same decode and the same tolerance as
+ * trellis_prefill; m outside [1, 4] returns TRELLIS_E_M. The pages' model
+ * code tells groups of at most TRELLIS_MATVEC_MAX_M rows (the matvec regime)
+ * from larger prefill groups (page "mlx-bun 0.4.0 -> 0.5.0" (npm diff,
+ * page 26), section src/model/qwen3_5.ts, mixed and layer-by-layer forward
+ * passes) and start the wide kernel at M = 5 (page 57,
+ * nativeTrellisWidePrefill); the limit's value is not printed, and 4 is the
+ * reading that leaves no gap. Each weight is used at most 4 times, so the
+ * call costs what the decode costs. */
+trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m,
+                              const uint32_t *codes, const uint16_t *scales_bf16,
+                              trellis_geom g, uint16_t *out_bf16, void *hip_stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *trellis_status_string(trellis_status s);

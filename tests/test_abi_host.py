@@ -116,3 +116,27 @@ def test_python_binding_raises_value_error_on_validation(lib):
         tp.prefill_raw(FAKE, 4, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)
     with pytest.raises(ValueError):
         tp.decode_raw(FAKE, FAKE, tp.geom(17408, 5120, 7), FAKE, 0)
+
+
+def call_matvec(x=FAKE, m=1, codes=FAKE, scales=FAKE, g=None, out=FAKE):
+    g = g or tp.geom(**GOOD)
+    return tp.load_library().trellis_matvec(x, m, codes, scales, g, out, None)
+
+
+def test_matvec_rejects_before_launch(lib):
+    assert call_matvec(g=tp.geom(17408, 5000, 4)) == tp.E_GEOMETRY
+    assert call_matvec(g=tp.geom(17408, 5120, 4, 256, 16)) == tp.E_GEOMETRY
+    for m in (0, -1, 5, 15):
+        assert call_matvec(m=m) == tp.E_M
+    assert call_matvec(x=None) == tp.E_NULL
+    assert call_matvec(codes=None) == tp.E_NULL
+    assert call_matvec(scales=None) == tp.E_NULL
+    assert call_matvec(out=None) == tp.E_NULL
+    assert call_matvec(x=FAKE + 2) == tp.E_ALIGN
+    assert call_matvec(codes=FAKE + 4) == tp.E_ALIGN
+    assert call_matvec(out=FAKE + 8) == tp.E_ALIGN
+    assert call_matvec(scales=FAKE + 1) == tp.E_ALIGN
+    assert call_matvec(g=tp.geom(17408, 5000, 4), m=5, x=None) == tp.E_GEOMETRY
+    assert call_matvec(m=5, x=None) == tp.E_M
+    with pytest.raises(ValueError):
+        tp.matvec_raw(FAKE, 5, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)

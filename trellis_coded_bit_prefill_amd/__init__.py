@@ -23,6 +23,7 @@ T_BLOCK = 256
 L_WINDOW = 12
 MIN_M = 5
 MAX_M = 15
+MATVEC_MAX_M = 4
 
 OK = 0
 E_GEOMETRY = -1
@@ -32,7 +33,7 @@ E_ALIGN = -4
 E_HIP = -5
 
 # Every symbol declared in include/trellis.h.
-EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_status_string")
+EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_decode.restype = ctypes.c_int
     L.trellis_prefill.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
     L.trellis_prefill.restype = ctypes.c_int
+    L.trellis_matvec.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
+    L.trellis_matvec.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -138,6 +141,12 @@ def prefill_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, ou
     _raise(load_library().trellis_prefill(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
 
 
+def matvec_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out_ptr: int,
+               stream: int) -> None:
+    """Direct C-ABI call with raw device addresses (1 <= m <= 4)."""
+    _raise(load_library().trellis_matvec(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
+
+
 @dataclass
 class Layer:
     """A packed Trellis linear layer: codes [N, K*bits/32] and scales [N]."""
@@ -176,7 +185,17 @@ def decode(codes, scales, k: int, bits: int, out=None):
 
 
 def prefill(x, codes, scales, bits: int, out=None):
-    """out[M, N] = x[M, K] . W^T (bf16), W decoded on the fly, current stream."""
+    """out[M, N] = x[M, K] . W^T (bf16), W decoded on the fly, current stream
+    (5 <= M <= 15)."""
+    return _linear(prefill_raw, x, codes, scales, bits, out)
+
+
+def matvec(x, codes, scales, bits: int, out=None):
+    """The same layer for 1 <= M <= 4 rows (decode tokens)."""
+    return _linear(matvec_raw, x, codes, scales, bits, out)
+
+
+def _linear(entry, x, codes, scales, bits: int, out=None):
     import torch
 
     bf, cw = _dtypes()
@@ -194,6 +213,6 @@ def prefill(x, codes, scales, bits: int, out=None):
     _check_tensor("out", out, bf, 2, x.device)
     if tuple(out.shape) != (m, n):
         raise ValueError("out must be [M, N]")
-    prefill_raw(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), geom(n, k, bits),
-                out.data_ptr(), _stream_handle(x.device))
+    entry(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), geom(n, k, bits), out.data_ptr(),
+          _stream_handle(x.device))
     return out

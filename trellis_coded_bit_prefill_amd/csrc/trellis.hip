@@ -856,7 +856,7 @@ const char *trellis_status_string(trellis_status s) {
   switch (s) {
     case TRELLIS_OK: return "ok";
     case TRELLIS_E_GEOMETRY: return "unsupported geometry (need t=256, l=12, bits 2/3/4, K%256==0, N%4==0)";
-    case TRELLIS_E_M: return "unsupported batch: m must be in [5, 15]";
+    case TRELLIS_E_M: return "unsupported batch: m must be in [5, 15] (prefill) or [1, 4] (matvec)";
     case TRELLIS_E_NULL: return "null pointer argument";
     case TRELLIS_E_ALIGN: return "misaligned pointer argument";
     case TRELLIS_E_HIP: return "HIP runtime error";
@@ -881,11 +881,15 @@ trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16
   return launch_status();
 }
 
-trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
-                               const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16,
-                               void *hip_stream) {
-  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
-  if (m < TRELLIS_MIN_M || m > TRELLIS_MAX_M) return TRELLIS_E_M;
+}  // extern "C"
+
+namespace trellis {
+namespace {
+
+// The fused layer for any 1 <= m <= 15 with a valid geometry (rows of A past
+// m are zero in LDS); the entry points below restrict m to their regimes.
+trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                             const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
   if (!x_bf16 || !codes || !scales_bf16 || !out_bf16) return TRELLIS_E_NULL;
   if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
     return TRELLIS_E_ALIGN;
@@ -936,6 +940,27 @@ trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t
       break;
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace trellis
+
+extern "C" {
+
+trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                               const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16,
+                               void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (m < TRELLIS_MIN_M || m > TRELLIS_MAX_M) return TRELLIS_E_M;
+  return launch_linear(x_bf16, m, codes, scales_bf16, g, out_bf16, hip_stream);
+}
+
+trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                              const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16,
+                              void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (m < 1 || m > TRELLIS_MATVEC_MAX_M) return TRELLIS_E_M;
+  return launch_linear(x_bf16, m, codes, scales_bf16, g, out_bf16, hip_stream);
 }
 
 }  // extern "C"

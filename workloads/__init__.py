@@ -63,6 +63,9 @@ SHAPES = {
     "wide_m8_k3": Shape("wide_m8_k3", 8, 5120, 17408, 3, 3),
     "wide_m15_k2": Shape("wide_m15_k2", 15, 5120, 17408, 2, 4),
     "down_m15_k4": Shape("down_m15_k4", 15, 17408, 5120, 4, 5, "silu_mul"),
+    # small-batch (matvec) regime, M = 1..4, on the wide geometry
+    "matvec_m1_k4": Shape("matvec_m1_k4", 1, 5120, 17408, 4, 6),
+    "matvec_m4_k2": Shape("matvec_m4_k2", 4, 5120, 17408, 2, 7),
 }
 
 
