@@ -568,6 +568,10 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // combine below.
   const int tf = tile;
   int tl = tile;  // the range's last tile
+  // Whether the range holds a tile shared with another workgroup (for one
+  // K panel only its first or last tile can be).
+  const bool holds_cross =
+      active && (cross(tf) || cross((int)((uint32_t)(u1 > 0 ? u1 - 1 : 0) / (uint32_t)pl.kp)));
   f32x4 part_f = {0.f, 0.f, 0.f, 0.f}, part_l = {0.f, 0.f, 0.f, 0.f};
   auto stage = [&](int t, f32x4 v) {
     stage_partial(partial_slot(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane), v);
@@ -586,8 +590,10 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     bool table_only = !__all(alu_scale_ok(s));
     const uint32_t mask_addr = PAIR ? 0xFFFCu : 0x3FFCu;  // table byte-address mask (SDWA operand)
     int u = u0;
-    // Decode unit u from slot C while unit u + 1 is requested into slot N.
-    auto step = [&](Slot &C, Slot &N) {
+    // Decode unit u from slot C while unit u + 1 is requested into slot N;
+    // the range's last unit requests nothing (`last`), so no load is left in
+    // flight after the loop.
+    auto step = [&](Slot &C, Slot &N, auto last) {
       if (tile != cur) {
         tile_done(cur, acc);
         cur = tile;
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         alu_row_constants(s, q, kq);
         table_only = !__all(alu_scale_ok(s));
       }
-      request(N);
+      if constexpr (!decltype(last)::value) request(N);
       const unsigned char *xb = xa + b * 512;
       // Rows whose scale is outside the exact range of code * q: the value
       // table (or, with the pair table, the ALU chain) for every group.
@@ -609,16 +615,24 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       // A SIMD issues from its highest-priority ready wave, oldest first
       // among equals; ranking waves by the units they have left lets the
       // younger waves catch up instead of running alone at the end.
-      const int rem = u1 - u;
+      // Pieces that hold tiles shared with other workgroups rank one level
+      // higher, so their partials are published before the others finish.
+      const int rem = u1 - u + (holds_cross && pl.panels == 1 ? 1 : 0);
       if (rem >= 3) __builtin_amdgcn_s_setprio(3);
       else if (rem == 2) __builtin_amdgcn_s_setprio(2);
       else __builtin_amdgcn_s_setprio(1);
     };
     for (;;) {
-      step(S0, S1);
-      if (u == u1) break;
-      step(S1, S0);
-      if (u == u1) break;
+      if (u + 1 == u1) {
+        step(S0, S1, std::true_type{});
+        break;
+      }
+      step(S0, S1, std::false_type{});
+      if (u + 1 == u1) {
+        step(S1, S0, std::true_type{});
+        break;
+      }
+      step(S1, S0, std::false_type{});
     }
     tl = cur;
     if (cross(cur)) stage(cur, acc);
@@ -634,7 +648,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // the counter. Its loads are issued only after its counter update
   // returned, and every other contributor's stores completed before its own
   // update, so no cache-wide fence is needed.
-  if (active) {
+  if (holds_cross) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     for (int t0 = tf; t0 <= tl; t0 += kWave) {
       const int t = t0 + lane;
