@@ -64,11 +64,18 @@ def cpu_baseline(shape, passes: int):
     import oracle
     from workloads import generate_shape
 
-    x, codes, scales = generate_shape(shape)
     oracle.lib()
+    if shape.matrices == 2:
+        from workloads import generate_gate_up
+
+        x, cg, sg, cu, su = generate_gate_up(shape)
+        run = lambda: oracle.gate_up_rows(x, cg, sg, cu, su, shape.k, shape.bits, range(shape.n))
+    else:
+        x, codes, scales = generate_shape(shape)
+        run = lambda: oracle.prefill_rows(x, codes, scales, shape.k, shape.bits, range(shape.n))
     t0 = time.perf_counter()
     for _ in range(passes):
-        oracle.prefill_rows(x, codes, scales, shape.k, shape.bits, range(shape.n))
+        run()
     dt = (time.perf_counter() - t0) / passes
     del np
     return {
@@ -121,41 +128,54 @@ def main():
     tp.load_library()
 
     # Input set 0 is the seeded workload; further sets (cold mode) draw the
-    # same distributions on the device from a fixed seed.
-    x0, c0, s0 = generate_shape(shape)
+    # same distributions on the device from a fixed seed. Each set holds x,
+    # (codes, scales) per weight matrix (gate and up for the fused tail), out.
     import numpy as np
+    from workloads import generate_gate_up
+
+    if shape.matrices == 2:
+        x0, cg0, sg0, cu0, su0 = generate_gate_up(shape)
+        mats0 = [(cg0, sg0), (cu0, su0)]
+    else:
+        x0, c0, s0 = generate_shape(shape)
+        mats0 = [(c0, s0)]
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    code_bytes = shape.n * shape.k * shape.bits // 8
+    code_bytes = shape.matrices * shape.n * shape.k * shape.bits // 8
     nsets = 1 if args.warm else max(2, -(-2 * MALL_BYTES // code_bytes))
     gen = torch.Generator(device=dev)
     gen.manual_seed(shape.seed * 1000 + 1)
     sets = []
     for i in range(nsets):
         if i == 0:
-            xs, cs, ss = dev_bf16(x0), torch.from_numpy(c0.view(np.int32)).to(dev), dev_bf16(s0)
+            xs = dev_bf16(x0)
+            mats = [(torch.from_numpy(c.view(np.int32)).to(dev), dev_bf16(sc)) for c, sc in mats0]
         else:
-            cs = torch.randint(-2 ** 31, 2 ** 31, c0.shape, dtype=torch.int32, device=dev, generator=gen)
             xs = torch.roll(sets[0][0], shifts=i, dims=1).contiguous()
-            ss = torch.roll(sets[0][2], shifts=i).contiguous()
+            mats = [(torch.randint(-2 ** 31, 2 ** 31, c.shape, dtype=torch.int32, device=dev, generator=gen),
+                     torch.roll(sets[0][1][mi][1], shifts=i).contiguous()) for mi, (c, _) in enumerate(mats0)]
         out = torch.empty((shape.m, shape.n), dtype=torch.bfloat16, device=dev)
-        sets.append((xs, cs, ss, out))
+        sets.append((xs, mats, out))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
     g = tp.geom(shape.n, shape.k, shape.bits)
-    ptrs = [(s[0].data_ptr(), s[1].data_ptr(), s[2].data_ptr(), s[3].data_ptr()) for s in sets]
+    ptrs = [(s[0].data_ptr(), [p.data_ptr() for cs in s[1] for p in cs], s[2].data_ptr()) for s in sets]
     lib = tp.load_library()
 
-    # M = 1..4 is the matvec entry point (same kernel and decode).
+    # M = 1..4 is the matvec entry point (same kernel and decode); two
+    # matrices are the fused gate/up entry point.
     entry = lib.trellis_matvec if shape.m < tp.MIN_M else lib.trellis_prefill
 
     def step(i):
-        xp, cp, sp, op = ptrs[i % nsets]
-        rc = entry(xp, shape.m, cp, sp, g, op, handle)
+        xp, mp, op = ptrs[i % nsets]
+        if shape.matrices == 2:
+            rc = lib.trellis_gate_up(xp, shape.m, mp[0], mp[1], mp[2], mp[3], g, op, handle)
+        else:
+            rc = entry(xp, shape.m, mp[0], mp[1], g, op, handle)
         if rc != 0:
             raise RuntimeError(tp.status_string(rc))
 
@@ -211,7 +231,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": shape.name, "m": shape.m, "k": shape.k, "n": shape.n, "bits": shape.bits,
-                   "T": 256, "L": 12, "input_sets": nsets, "mode": "warm" if args.warm else "cold"},
+                   "T": 256, "L": 12, "matrices": shape.matrices, "input_sets": nsets,
+                   "mode": "warm" if args.warm else "cold"},
         "gweights_per_s": round(shape.weights / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {
             "bound": "hbm",

@@ -41,12 +41,13 @@
  *
  * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns without waiting. trellis_decode keeps no
- * state. trellis_prefill sums tiles that are split across workgroups
- * through a workspace (float32 partial tiles and per-tile counters) owned by
- * the library, one per (device, stream): it is allocated with hipMalloc on
- * the first call that needs it, grown (never shrunk or freed) when a later
- * call on that stream needs more, and kept until the process exits; the
- * kernel leaves its counters at zero for the next call. Calls on different
+ * state. trellis_prefill, trellis_matvec and trellis_gate_up sum tiles that
+ * are split across workgroups through a workspace (float32 partial tiles
+ * and per-tile counters; for trellis_gate_up also the two bf16 projections)
+ * owned by the library, one per (device, stream): it is allocated with
+ * hipMalloc on the first call that needs it, grown (never shrunk or freed)
+ * when a later call on that stream needs more, and kept until the process
+ * exits; the kernel leaves its counters at zero for the next call. Calls on different
  * streams therefore never share a workspace; calls on one stream are
  * ordered by the stream. Host-side state is guarded by a mutex, so calls
  * may come from several threads. Errors are returned, never thrown; a
@@ -122,6 +123,21 @@ trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m,
 trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m,
                               const uint32_t *codes, const uint16_t *scales_bf16,
                               trellis_geom g, uint16_t *out_bf16, void *hip_stream);
+
+/* The MLP's gate and up projections of one x, fused:
+ *   h[M, N] = bf16(bf16(gate * bf16(sigmoid(gate))) * up),
+ *   gate = bf16(x . Wg^T), up = bf16(x . Wu^T),
+ * following the page's model code, where each step yields a bf16 array
+ * (page "mlx-bun 0.0.4" (npm, page 62), section src/model/minicpm5.ts, MLP
+ * forward); sigmoid is evaluated in float32. Wg and Wu share the geometry g
+ * (same N, K and bits) and the formats above; 1 <= m <= 15. One launch
+ * decodes both code streams against one staging of x into two bf16
+ * projections held in the library's per-stream scratch (M x 32*ceil(N/16)
+ * values), and a second, elementwise launch writes h. */
+trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m,
+                               const uint32_t *codes_gate, const uint16_t *scales_gate,
+                               const uint32_t *codes_up, const uint16_t *scales_up,
+                               trellis_geom g, uint16_t *h_bf16, void *hip_stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *trellis_status_string(trellis_status s);

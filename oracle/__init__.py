@@ -216,3 +216,50 @@ def within_tolerance(out_bf16_bits: np.ndarray, y: np.ndarray, a: np.ndarray, re
     out = (np.asarray(out_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     out = out.astype(np.float64)
     return np.abs(out - y) <= ulp_bf16(out) + rel * a
+
+
+# ---- gate/up tail of an MLP ------------------------------------------------
+# Page "mlx-bun 0.0.4" (npm, page 62), section src/model/minicpm5.ts, MLP
+# forward: gate and up projections of the same x, then
+# hidden = (gate * sigmoid(gate)) * up.
+
+def silu(g):
+    """g * sigmoid(g) = g / (1 + exp(-g)) in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def gate_up_rows(x, codes_g, scales_g, codes_u, scales_u, k: int, bits: int, rows):
+    """Float64 reference of the fused gate/up tail for output columns `rows`.
+
+    Returns (h, g, ag, u, au): g and u are the float64 sums of the same bf16
+    products (prefill_rows), ag and au their sums of |w*x|, and
+    h = silu(g) * u with no intermediate rounding.
+    """
+    g, ag = prefill_rows(x, codes_g, scales_g, k, bits, rows)
+    u, au = prefill_rows(x, codes_u, scales_u, k, bits, rows)
+    return silu(g) * u, g, ag, u, au
+
+
+def gate_up_within_tolerance(h_bf16_bits, h, g, ag, u, au, rel: float = 1e-5):
+    """Boolean mask: the device's h is within the bound the page's bf16 chain
+    allows around the exact h = silu(g) * u.
+
+    The device rounds gate and up to bf16 after float32 accumulation, each
+    within Eg = 2 ulp_bf16(g) + rel*ag of g (resp. Eu of u), then rounds
+    sigmoid(gate), gate*sigmoid(gate) and that times up to bf16. With
+    |silu'| <= 1.1, S = |silu(g)| + 1.1 Eg and V = |u| + Eu bound the rounded
+    operands, so
+      |h_dev - h| <= (1.1 Eg + 2^-7 S) V + |silu(g)| Eu + 2^-8 S V + 2^-133,
+    where 2^-7 S covers the two roundings inside silu and 2^-8 S V the last
+    one (each at most half an ulp, i.e. 2^-9 relative, doubled for margin).
+    """
+    hd = (np.asarray(h_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    eg = 2 * ulp_bf16(g) + rel * ag
+    eu = 2 * ulp_bf16(u) + rel * au
+    sg = np.abs(silu(g))
+    s = sg + 1.1 * eg
+    v = np.abs(u) + eu
+    bound = (1.1 * eg + 2.0 ** -7 * s) * v + sg * eu + 2.0 ** -8 * s * v + 2.0 ** -133
+    return np.abs(hd - h) <= bound

@@ -140,3 +140,26 @@ def test_matvec_rejects_before_launch(lib):
     assert call_matvec(m=5, x=None) == tp.E_M
     with pytest.raises(ValueError):
         tp.matvec_raw(FAKE, 5, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)
+
+
+def call_gate_up(x=FAKE, m=5, cg=FAKE, sg=FAKE, cu=FAKE, su=FAKE, g=None, h=FAKE):
+    g = g or tp.geom(**GOOD)
+    return tp.load_library().trellis_gate_up(x, m, cg, sg, cu, su, g, h, None)
+
+
+def test_gate_up_rejects_before_launch(lib):
+    assert call_gate_up(g=tp.geom(17408, 5000, 4)) == tp.E_GEOMETRY
+    for m in (0, 16, -3):
+        assert call_gate_up(m=m) == tp.E_M
+    for kw in ("x", "cg", "sg", "cu", "su", "h"):
+        assert call_gate_up(**{kw: None}) == tp.E_NULL, kw
+    assert call_gate_up(x=FAKE + 2) == tp.E_ALIGN
+    assert call_gate_up(cg=FAKE + 4) == tp.E_ALIGN
+    assert call_gate_up(cu=FAKE + 4) == tp.E_ALIGN
+    assert call_gate_up(sg=FAKE + 1) == tp.E_ALIGN
+    assert call_gate_up(su=FAKE + 1) == tp.E_ALIGN
+    assert call_gate_up(h=FAKE + 8) == tp.E_ALIGN
+    assert call_gate_up(g=tp.geom(17408, 5000, 4), m=0, x=None) == tp.E_GEOMETRY
+    assert call_gate_up(m=0, x=None) == tp.E_M
+    with pytest.raises(ValueError):
+        tp.gate_up_raw(FAKE, 16, FAKE, FAKE, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)

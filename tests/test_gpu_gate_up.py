@@ -1,0 +1,87 @@
+"""GPU parity of trellis_gate_up against the CPU oracle.
+
+h = silu(x . Wg^T) * (x . Wu^T) with the page's bf16 roundings of every
+intermediate array. The reference is the exact float64 h = silu(g) * u of
+the float64 projections; the bound (oracle.gate_up_within_tolerance) carries
+the projections' tolerance through silu and the product and adds the chain's
+three bf16 roundings.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import trellis_coded_bit_prefill_amd as tp
+from tests.helpers import from_dev_bf16, to_dev_bf16, to_dev_codes
+from workloads import SHAPES, generate, generate_gate_up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tp.load_library()
+
+
+def gpu_gate_up(x, cg, sg, cu, su, bits):
+    import torch
+
+    h = tp.gate_up(to_dev_bf16(x), to_dev_codes(cg), to_dev_bf16(sg), to_dev_codes(cu), to_dev_bf16(su), bits)
+    torch.cuda.synchronize()
+    return from_dev_bf16(h)
+
+
+def check(h, x, cg, sg, cu, su, k, bits, rows, what):
+    ref, g, ag, u, au = oracle.gate_up_rows(x, cg, sg, cu, su, k, bits, rows)
+    ok = oracle.gate_up_within_tolerance(h[:, rows], ref, g, ag, u, au)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        hv = (h[:, rows].astype(np.uint32) << 16).view(np.float32)
+        detail = ", ".join(f"[{i},{j}] gpu={hv[i, j]!r} ref={ref[i, j]!r} g={g[i, j]!r} u={u[i, j]!r}"
+                           for i, j in idx)
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} out of bound: {detail}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("m", [1, 5, 15])
+@pytest.mark.parametrize("n,k", [(4, 256), (68, 768), (324, 1792)])
+def test_gate_up_small_shapes(bits, m, n, k):
+    print(f"gate_up small m={m} n={n} k={k} bits={bits}", flush=True)
+    x, cg, sg = generate(m, k, n, bits, seed=7000 + 7 * m + n + k + bits)
+    _, cu, su = generate(m, k, n, bits, seed=8000 + 7 * m + n + k + bits)
+    h = gpu_gate_up(x, cg, sg, cu, su, bits)
+    assert h.shape == (m, n)
+    check(h, x, cg, sg, cu, su, k, bits, np.arange(n), f"m={m} n={n} k={k} bits={bits}")
+
+
+def test_gate_up_full_shape():
+    s = SHAPES["gateup_m5_k4"]
+    print("gate_up full shape", flush=True)
+    x, cg, sg, cu, su = generate_gate_up(s)
+    h = gpu_gate_up(x, cg, sg, cu, su, s.bits)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(s.n - 64, s.n), rng.integers(0, s.n, 384)]))
+    check(h, x, cg, sg, cu, su, s.k, s.bits, rows, s.name)
+
+
+def test_gate_up_k_panels():
+    # x too large for one LDS panel: every tile of both matrices is summed
+    # across workgroups before the elementwise tail.
+    print("gate_up k panels", flush=True)
+    m, k, n, bits = 15, 17408, 260, 4
+    x, cg, sg = generate(m, k, n, bits, seed=9001, x_kind="silu_mul")
+    _, cu, su = generate(m, k, n, bits, seed=9002)
+    h = gpu_gate_up(x, cg, sg, cu, su, bits)
+    check(h, x, cg, sg, cu, su, k, bits, np.arange(n), "k panels")
+
+
+def test_gate_up_deterministic():
+    m, k, n, bits = 8, 1024, 196, 3
+    x, cg, sg = generate(m, k, n, bits, seed=9101)
+    _, cu, su = generate(m, k, n, bits, seed=9102)
+    a = gpu_gate_up(x, cg, sg, cu, su, bits)
+    b = gpu_gate_up(x, cg, sg, cu, su, bits)
+    assert np.array_equal(a, b)

@@ -381,3 +381,69 @@ def test_ulp_bf16():
     out = torch_bf16_bits([1.0, 2.0])
     assert oracle.within_tolerance(out, np.array([1.0 + 2 ** -7, 2.0 - 2 ** -6]), np.zeros(2)).all()
     assert not oracle.within_tolerance(out, np.array([1.0 + 2 ** -6, 2.0]), np.zeros(2))[0]
+
+
+# ---- gate/up tail (silu(gate) * up) ------------------------------------------
+
+def test_silu_closed_forms():
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly; silu(0) = 0;
+    # silu(x) - silu(-x) = x for every x; silu(x) -> x and -> 0 at the ends.
+    ln3 = np.log(3.0)
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(ln3) - 0.75 * ln3) <= 1e-15
+    assert abs(oracle.silu(-ln3) + 0.25 * ln3) <= 1e-15
+    xs = np.linspace(-30, 30, 601)
+    assert np.allclose(oracle.silu(xs) - oracle.silu(-xs), xs, rtol=0, atol=1e-13)
+    assert abs(oracle.silu(60.0) - 60.0) <= 1e-20 * 60 + 1e-12
+    assert abs(oracle.silu(-800.0)) == 0.0
+    # minimum of silu: about -0.2785 at x about -1.2785 (x = -1 - W(1/e))
+    grid = np.linspace(-3, 0, 300001)
+    assert abs(oracle.silu(grid).min() + 0.27846454276) < 1e-9
+
+
+def test_gate_up_rows_one_hot_and_zero_codes():
+    # One-hot x rows: g = Wg[n, j], u = Wu[n, j], so h = silu(Wg[n, j]) * Wu[n, j];
+    # all-zero up codes: u = w0(n) * sum(x) as in the prefill closed form.
+    from workloads import generate
+
+    k, n = 512, 12
+    _, cg, sg = generate(5, k, n, 4, seed=21)
+    _, cu, su = generate(5, k, n, 4, seed=22)
+    js = [0, 7, 256, 511]
+    x = np.zeros((len(js), k), dtype=np.uint16)
+    x[np.arange(len(js)), js] = 0x3F80
+    h, g, ag, u, au = oracle.gate_up_rows(x, cg, sg, cu, su, k, 4, range(n))
+    wg = bf16_value(oracle.decode(cg, sg, k, 4)).astype(np.float64)
+    wu = bf16_value(oracle.decode(cu, su, k, 4)).astype(np.float64)
+    for i, j in enumerate(js):
+        assert np.array_equal(g[i], wg[:, j]) and np.array_equal(u[i], wu[:, j])
+        assert np.allclose(h[i], wg[:, j] / (1 + np.exp(-wg[:, j])) * wu[:, j], rtol=1e-15, atol=0)
+    xr, _, _ = generate(3, k, n, 4, seed=23)
+    hz, gz, _, uz, _ = oracle.gate_up_rows(xr, cg, sg, np.zeros_like(cu), su, k, 4, range(n))
+    yz, _ = oracle.prefill(xr, np.zeros_like(cu), su, k, 4)
+    assert np.array_equal(uz, yz)
+
+
+def test_gate_up_tolerance_accepts_the_chain_and_rejects_a_slip():
+    # The bf16 chain applied to bf16-rounded g, u lies inside the bound; an
+    # output one bf16 step from it for |h| well above the bound does not.
+    rng = np.random.default_rng(31)
+    g = rng.normal(0, 2, 2000)
+    u = rng.normal(0, 2, 2000)
+    ag = np.abs(g) * 3
+    au = np.abs(u) * 3
+    gb = bf16_value(torch_bf16_bits(g.astype(np.float32))).astype(np.float64)
+    ub = bf16_value(torch_bf16_bits(u.astype(np.float32))).astype(np.float64)
+    sig = bf16_value(torch_bf16_bits((1 / (1 + np.exp(-gb))).astype(np.float32))).astype(np.float64)
+    silu_b = bf16_value(torch_bf16_bits((gb * sig).astype(np.float32))).astype(np.float64)
+    hb = torch_bf16_bits((silu_b * ub).astype(np.float32))
+    h = oracle.silu(g) * u
+    assert oracle.gate_up_within_tolerance(hb, h, g, ag, u, au).all()
+    # the rounding terms alone cover the chain (no accumulation error here)
+    assert oracle.gate_up_within_tolerance(hb, h, g, np.zeros_like(ag), u, np.zeros_like(au)).all()
+    far = torch_bf16_bits((bf16_value(hb).astype(np.float64) * 1.25).astype(np.float32))
+    # where silu is not tiny next to its slope (gate >= 0.5) the bound is a
+    # few percent of |h|, so a 25% slip must fail
+    sel = (g >= 0.5) & (np.abs(h) > 0.5)
+    assert sel.sum() > 100
+    assert not oracle.gate_up_within_tolerance(far, h, g, np.zeros_like(ag), u, np.zeros_like(au))[sel].any()

@@ -33,7 +33,8 @@ E_ALIGN = -4
 E_HIP = -5
 
 # Every symbol declared in include/trellis.h.
-EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_status_string")
+EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_gate_up",
+            "trellis_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_prefill.restype = ctypes.c_int
     L.trellis_matvec.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
     L.trellis_matvec.restype = ctypes.c_int
+    L.trellis_gate_up.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, Geom, vp, vp]
+    L.trellis_gate_up.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -145,6 +148,13 @@ def matvec_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out
                stream: int) -> None:
     """Direct C-ABI call with raw device addresses (1 <= m <= 4)."""
     _raise(load_library().trellis_matvec(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
+
+
+def gate_up_raw(x_ptr: int, m: int, codes_gate_ptr: int, scales_gate_ptr: int, codes_up_ptr: int,
+                scales_up_ptr: int, g: Geom, h_ptr: int, stream: int) -> None:
+    """Direct C-ABI call with raw device addresses (1 <= m <= 15)."""
+    _raise(load_library().trellis_gate_up(x_ptr, m, codes_gate_ptr, scales_gate_ptr, codes_up_ptr,
+                                          scales_up_ptr, g, h_ptr, stream))
 
 
 @dataclass
@@ -215,4 +225,32 @@ def _linear(entry, x, codes, scales, bits: int, out=None):
         raise ValueError("out must be [M, N]")
     entry(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), geom(n, k, bits), out.data_ptr(),
           _stream_handle(x.device))
+    return out
+
+
+def gate_up(x, codes_gate, scales_gate, codes_up, scales_up, bits: int, out=None):
+    """h[M, N] = silu(x . Wg^T) * (x . Wu^T) with the page's bf16 roundings,
+    both weight matrices decoded on the fly in one pass (1 <= M <= 15)."""
+    import torch
+
+    bf, cw = _dtypes()
+    _check_tensor("x", x, bf, 2)
+    for name, c, sc in (("gate", codes_gate, scales_gate), ("up", codes_up, scales_up)):
+        _check_tensor(f"codes_{name}", c, cw, 2, x.device)
+        _check_tensor(f"scales_{name}", sc, bf, 1, x.device)
+    m, k = x.shape
+    n = codes_gate.shape[0]
+    if tuple(codes_up.shape) != tuple(codes_gate.shape):
+        raise ValueError("gate and up codes must have the same shape")
+    if codes_gate.shape[1] * 32 != k * bits:
+        raise ValueError(f"codes have {codes_gate.shape[1]} words per row, expected K*bits/32 = {k * bits // 32}")
+    if scales_gate.shape[0] != n or scales_up.shape[0] != n:
+        raise ValueError("scales must have one entry per row")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check_tensor("out", out, bf, 2, x.device)
+    if tuple(out.shape) != (m, n):
+        raise ValueError("out must be [M, N]")
+    gate_up_raw(x.data_ptr(), m, codes_gate.data_ptr(), scales_gate.data_ptr(), codes_up.data_ptr(),
+                scales_up.data_ptr(), geom(n, k, bits), out.data_ptr(), _stream_handle(x.device))
     return out

@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
 // Work partition, computed on the host and re-derived by every wave.
 struct Plan {
   int32_t m, n, k;
-  int32_t tiles;     // ceil(N / 16)
+  int32_t tiles;     // ceil(N / 16), or twice that for two matrices
+  int32_t half;      // two matrices: tiles of the first (the second's start); 0 for one
+  int32_t out_rows;  // columns of out (its row stride): N, or 32 * half for two matrices
   int32_t panels;    // K panels (x panel staged per workgroup)
   int32_t kp;        // 256-weight blocks per panel
   int32_t groups;    // workgroups per panel
@@ -440,6 +442,8 @@ template <int BITS, int MASK, bool PAIR>
 __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__restrict__ x,
                                                              const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
+                                                             const uint32_t *__restrict__ codes2,
+                                                             const uint16_t *__restrict__ scales2,
                                                              uint16_t *__restrict__ out, float *__restrict__ ws,
                                                              uint32_t *__restrict__ counters, Plan pl) {
   // The table is static LDS (address known at compile time, so table reads
@@ -479,18 +483,24 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   const uint32_t lane_off_scale = (uint32_t)j * 2;
   // Buffers of unit (t, bb) and of tile t's scales: rows past N are outside
   // them, so their words and scales read as zero (zero weights, never stored).
+  // With two matrices (gate and up), tiles [half, tiles) are the second
+  // matrix's tiles 0, 1, ...
   auto unit_buffer = [&](int t, int bb) {
-    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
+    const bool second = pl.half > 0 && t >= pl.half;
+    const int tt = second ? t - pl.half : t;
+    const int rows = pl.n - tt * 16 < 16 ? pl.n - tt * 16 : 16;
     const uint32_t blk_off = (uint32_t)(panel * pl.kp + bb) * (wpb * 4);
-    const unsigned char *base = reinterpret_cast<const unsigned char *>(codes) +
-                                (int64_t)t * 16 * row_bytes + blk_off;
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(second ? codes2 : codes) +
+                                (int64_t)tt * 16 * row_bytes + blk_off;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(base), (short)0,
                                              (int)((uint32_t)rows * row_bytes - blk_off), kRawBufferWord3);
   };
   auto scale_buffer = [&](int t) {
-    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales + (int64_t)t * 16), (short)0,
-                                             rows * 2, kRawBufferWord3);
+    const bool second = pl.half > 0 && t >= pl.half;
+    const int tt = second ? t - pl.half : t;
+    const int rows = pl.n - tt * 16 < 16 ? pl.n - tt * 16 : 16;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((second ? scales2 : scales) + (int64_t)tt * 16),
+                                             (short)0, rows * 2, kRawBufferWord3);
   };
   // Raw scale bits are converted only when the tile starts, so the load is
   // not waited for early.
@@ -580,7 +590,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   auto tile_done = [&](int t, f32x4 v) {
     if (cross(t)) stage(t, v);
     else if (t == tf && u0 > t * pl.kp) part_f = v;
-    else store_tile(out, v, pl.m, pl.n, t * 16 + j, g);
+    else store_tile(out, v, pl.m, pl.out_rows, t * 16 + j, g);
   };
   if (active) {
     int cur = tile;
@@ -636,7 +646,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     }
     tl = cur;
     if (cross(cur)) stage(cur, acc);
-    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(out, acc, pl.m, pl.n, cur * 16 + j, g);
+    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(out, acc, pl.m, pl.out_rows, cur * 16 + j, g);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
@@ -665,7 +675,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         last &= last - 1;
         const int T = t0 + i;
         const int c = __shfl(contrib, i);
-        store_tile(out, sum_partials(pl, ws, T, c, lane), pl.m, pl.n, T * 16 + j, g);
+        store_tile(out, sum_partials(pl, ws, T, c, lane), pl.m, pl.out_rows, T * 16 + j, g);
         if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -710,8 +720,28 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
       if (e >= t1u) break;  // T ends in this segment
     }
-    store_tile(out, sum, pl.m, pl.n, T * 16 + j, g);
+    store_tile(out, sum, pl.m, pl.out_rows, T * 16 + j, g);
   }
+}
+
+// ---------------------------------------------------------------------------
+// gate_up_kernel: the MLP's elementwise tail on the two projections, as the
+// page's model code orders it (page "mlx-bun 0.0.4" (npm, page 62), section
+// src/model/minicpm5.ts, MLP forward): every operation yields a bf16 array,
+// so sigmoid(gate), gate * sigmoid(gate) and that times up are each rounded
+// to bf16. gu holds row i's gate values at [i * 2h, i * 2h + n) and its up
+// values at [i * 2h + h, ...), h = half_rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t *__restrict__ gu, int m, int n, int half_rows,
+                                                      uint16_t *__restrict__ h) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)m * n) return;
+  const int i = (int)(idx / n), c = (int)(idx - (int64_t)i * n);
+  const uint16_t *row = gu + (int64_t)i * 2 * half_rows;
+  const float gate = bf16_bits_to_f32(row[c]), up = bf16_bits_to_f32(row[half_rows + c]);
+  const float sig = (float)(__bf16)(1.0f / (1.0f + expf(-gate)));
+  const float silu = (float)(__bf16)(gate * sig);
+  h[idx] = __builtin_bit_cast(uint16_t, (__bf16)(silu * up));
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
@@ -741,12 +771,15 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 void clear_last_error() { (void)hipGetLastError(); }
 trellis_status launch_status() { return hipGetLastError() == hipSuccess ? TRELLIS_OK : TRELLIS_E_HIP; }
 
-Plan make_plan(int m, int n, int k, int cus, int table) {
+Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   Plan pl{};
   pl.m = m;
   pl.n = n;
   pl.k = k;
-  pl.tiles = (n + 15) / 16;
+  const int tiles = (n + 15) / 16;
+  pl.tiles = two ? 2 * tiles : tiles;
+  pl.half = two ? tiles : 0;
+  pl.out_rows = two ? 32 * tiles : n;
   const int kb = k / 256;
   int panels = kb;
   for (int p = 1; p <= kb; ++p) {
@@ -798,6 +831,8 @@ struct Workspace {
   size_t ws_floats = 0;
   uint32_t *counters = nullptr;
   size_t ncounters = 0;
+  uint16_t *gu = nullptr;  // gate and up projections (bf16) of trellis_gate_up
+  size_t gu_elems = 0;
 };
 
 std::mutex g_mu;
@@ -855,6 +890,15 @@ trellis_status workspace(hipStream_t stream, size_t ws_floats, size_t ncounters,
   return TRELLIS_OK;
 }
 
+trellis_status gate_up_scratch(Workspace &w, size_t elems) {
+  if (w.gu_elems >= elems) return TRELLIS_OK;
+  uint16_t *p = nullptr;
+  if (hipMalloc(&p, elems * sizeof(uint16_t)) != hipSuccess) return TRELLIS_E_HIP;
+  w.gu = p;
+  w.gu_elems = elems;
+  return TRELLIS_OK;
+}
+
 }  // namespace
 }  // namespace trellis
 
@@ -901,12 +945,17 @@ namespace trellis {
 namespace {
 
 // The fused layer for any 1 <= m <= 15 with a valid geometry (rows of A past
-// m are zero in LDS); the entry points below restrict m to their regimes.
+// m are zero in LDS); the entry points restrict m to their regimes. With a
+// second matrix (codes2, scales2), both projections go through one launch
+// into the gate/up scratch and gate_up_kernel writes out = silu(gate) * up.
 trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
-                             const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
-  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16) return TRELLIS_E_NULL;
+                             const uint16_t *scales_bf16, const uint32_t *codes2, const uint16_t *scales2,
+                             trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
+  const bool two = codes2 != nullptr || scales2 != nullptr;
+  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16 || (two && (!codes2 || !scales2))) return TRELLIS_E_NULL;
   if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
     return TRELLIS_E_ALIGN;
+  if (two && (!aligned(codes2, 16) || !aligned(scales2, 2))) return TRELLIS_E_ALIGN;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   std::lock_guard<std::mutex> lock(g_mu);
   int cus = 0;
@@ -919,9 +968,9 @@ trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *
   // k = 2 uses the pair table unless its larger footprint would split x
   // into more K panels than the value table does.
   Variant v = g.bits == 3 ? kK3 : g.bits == 4 ? kK4 : kK2;
-  Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(false));
+  Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(false), two);
   if (v == kK2) {
-    const Plan pp = make_plan(m, g.n, g.k, cus, table_bytes(true));
+    const Plan pp = make_plan(m, g.n, g.k, cus, table_bytes(true), two);
     if (pp.panels == pl.panels) {
       pl = pp;
       v = kK2Pair;
@@ -933,25 +982,36 @@ trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *
   Workspace *w = nullptr;
   rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256, (size_t)pl.tiles, w);
   if (rc != TRELLIS_OK) return rc;
+  uint16_t *dst = out_bf16;
+  if (two) {
+    rc = gate_up_scratch(*w, (size_t)m * pl.out_rows);
+    if (rc != TRELLIS_OK) return rc;
+    dst = w->gu;
+  }
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
   switch (v) {
     case kK2:
       hipLaunchKernelGGL((prefill_kernel<2, Mix<2>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
+                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
       break;
     case kK3:
       hipLaunchKernelGGL((prefill_kernel<3, Mix<3>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
+                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
       break;
     case kK4:
       hipLaunchKernelGGL((prefill_kernel<4, Mix<4>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
+                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
       break;
     default:
       hipLaunchKernelGGL((prefill_kernel<2, Mix<2, true>::kMask, true>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, out_bf16, w->ws, w->counters, pl);
+                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
       break;
+  }
+  if (two) {
+    const int64_t total = (int64_t)m * g.n;
+    hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       (const uint16_t *)dst, m, g.n, pl.half * 16, out_bf16);
   }
   return launch_status();
 }
@@ -966,7 +1026,7 @@ trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m, const uint32_t
                                void *hip_stream) {
   if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
   if (m < TRELLIS_MIN_M || m > TRELLIS_MAX_M) return TRELLIS_E_M;
-  return launch_linear(x_bf16, m, codes, scales_bf16, g, out_bf16, hip_stream);
+  return launch_linear(x_bf16, m, codes, scales_bf16, nullptr, nullptr, g, out_bf16, hip_stream);
 }
 
 trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
@@ -974,7 +1034,16 @@ trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m, const uint32_t 
                               void *hip_stream) {
   if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
   if (m < 1 || m > TRELLIS_MATVEC_MAX_M) return TRELLIS_E_M;
-  return launch_linear(x_bf16, m, codes, scales_bf16, g, out_bf16, hip_stream);
+  return launch_linear(x_bf16, m, codes, scales_bf16, nullptr, nullptr, g, out_bf16, hip_stream);
+}
+
+trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m, const uint32_t *codes_gate,
+                               const uint16_t *scales_gate, const uint32_t *codes_up, const uint16_t *scales_up,
+                               trellis_geom g, uint16_t *h_bf16, void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (m < 1 || m > TRELLIS_MAX_M) return TRELLIS_E_M;
+  if (!codes_up || !scales_up) return TRELLIS_E_NULL;
+  return launch_linear(x_bf16, m, codes_gate, scales_gate, codes_up, scales_up, g, h_bf16, hip_stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,7 @@ class Shape:
     bits: int
     seed: int
     x_kind: str = "rmsnorm"   # "rmsnorm" or "silu_mul"
+    matrices: int = 1         # 2: gate and up projections of the same x
 
     @property
     def words_per_row(self) -> int:
@@ -47,12 +48,12 @@ class Shape:
 
     @property
     def weights(self) -> int:
-        return self.n * self.k
+        return self.matrices * self.n * self.k
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Packed code bytes + bf16 x + bf16 out (scales excluded)."""
-        return self.n * self.k * self.bits // 8 + 2 * self.m * self.k + 2 * self.m * self.n
+        """Packed code bytes (every matrix) + bf16 x + bf16 out (scales excluded)."""
+        return self.matrices * self.n * self.k * self.bits // 8 + 2 * self.m * self.k + 2 * self.m * self.n
 
 
 # The five workloads: a tiny shape, the wide K=5120 x N=17408 shape at three
@@ -66,6 +67,8 @@ SHAPES = {
     # small-batch (matvec) regime, M = 1..4, on the wide geometry
     "matvec_m1_k4": Shape("matvec_m1_k4", 1, 5120, 17408, 4, 6),
     "matvec_m4_k2": Shape("matvec_m4_k2", 4, 5120, 17408, 2, 7),
+    # fused gate + up projections of one x (two code streams of this geometry)
+    "gateup_m5_k4": Shape("gateup_m5_k4", 5, 5120, 17408, 4, 8, "rmsnorm", 2),
 }
 
 
@@ -116,3 +119,12 @@ def generate(m: int, k: int, n: int, bits: int, seed: int, x_kind: str = "rmsnor
 
 def generate_shape(shape: Shape, m: int | None = None):
     return generate(shape.m if m is None else m, shape.k, shape.n, shape.bits, shape.seed, shape.x_kind)
+
+
+def generate_gate_up(shape: Shape):
+    """x and the gate matrix as generate_shape(shape); the up matrix's codes
+    and scales drawn the same way from seed + 1000.
+    Returns (x, codes_gate, scales_gate, codes_up, scales_up)."""
+    x, cg, sg = generate_shape(shape)
+    _, cu, su = generate(shape.m, shape.k, shape.n, shape.bits, shape.seed + 1000, shape.x_kind)
+    return x, cg, sg, cu, su
