@@ -165,3 +165,18 @@ def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift):
         ref = (w_ref[:, cols].T.astype(np.uint32) << 16).view(np.float32)
         bad += int(np.sum(got != ref))  # +0 == -0: zero weights may differ in sign only
     assert bad == 0
+
+
+def test_prefill_workspace_grows_between_calls():
+    # One stream: a small call, a call needing a larger workspace (more tiles,
+    # K panels), then the small call again; the grown workspace starts with
+    # zeroed counters and every result stays within the tolerance.
+    cases = [(5, 512, 256, 2, 21), (15, 17408, 1040, 4, 22), (8, 768, 68, 3, 23), (15, 17408, 1040, 4, 24)]
+    for m, k, n, bits, seed in cases:
+        print(f"prefill workspace growth m={m} k={k} n={n} bits={bits}", flush=True)
+        x, codes, scales = generate(m, k, n, bits, seed=seed)
+        out = gpu_prefill(x, codes, scales, bits)
+        rows = np.arange(n) if n <= 400 else np.unique(np.concatenate([np.arange(40), np.arange(n - 40, n),
+                                                                        np.arange(0, n, 37)]))
+        y, a = oracle.prefill_rows(x, codes, scales, k, bits, rows)
+        assert_prefill_close(out[:, rows], y, a, f"growth m={m} k={k} n={n}")

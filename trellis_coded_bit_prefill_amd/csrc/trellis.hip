@@ -724,6 +724,11 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   }
 }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // gate_up_kernel: the MLP's elementwise tail on the two projections, as the
 // page's model code orders it (page "mlx-bun 0.0.4" (npm, page 62), section
@@ -882,7 +887,11 @@ trellis_status workspace(hipStream_t stream, size_t ws_floats, size_t ncounters,
   if (w.ncounters < ncounters) {
     uint32_t *c = nullptr;
     if (hipMalloc(&c, ncounters * sizeof(uint32_t)) != hipSuccess) return TRELLIS_E_HIP;
-    if (hipMemsetAsync(c, 0, ncounters * sizeof(uint32_t), stream) != hipSuccess) return TRELLIS_E_HIP;
+    // Zeroed by a kernel on the stream, ordered before the first use (a
+    // memset node would be unsafe if a caller captured the stream).
+    const dim3 grid((unsigned)((ncounters + 255) / 256));
+    hipLaunchKernelGGL(zero_u32_kernel, grid, dim3(256), 0, stream, c, (int64_t)ncounters);
+    if (hipGetLastError() != hipSuccess) return TRELLIS_E_HIP;
     w.counters = c;
     w.ncounters = ncounters;
   }
