@@ -5,21 +5,27 @@
 // 1MAD hash, byte sum, reciprocal-refinement normalisation, per-row scale,
 // bf16 rounding, narrow-M dot product) and host wrapper (shape checks). The
 // materialising decode is the "expand" mode of page "mlx-bun 0.4.0 -> 0.5.0"
-// (npm diff, page 26), section src/model/trellis-linear.ts.
+// (npm diff, page 26), section src/model/trellis-linear.ts. The fused gate/up
+// tail follows page "mlx-bun 0.0.4" (npm, page 62), section
+// src/model/minicpm5.ts (MLP forward).
 //
 // CDNA4 design (not a translation of the Metal kernel):
-//   * one persistent workgroup per CU; the work is a list of units (16-row
-//     tile x one 256-weight block) split into equal contiguous ranges per
-//     wave (stream-K), so every SIMD gets the same decode work;
+//   * one persistent workgroup of 16 waves per CU; the work is a list of
+//     units (16-row tile x one 256-weight block), split evenly over
+//     workgroups and then into 16 contiguous pieces whose lengths differ by at
+//     most one unit per SIMD (stream-K); waves rank themselves by the work
+//     they have left;
 //   * x is staged once per workgroup in LDS (a K panel of it when all of x
 //     does not fit) with an all-zero row that pads M up to 16;
-//   * each lane loads the code words of 64 consecutive weights of one row
-//     (coalesced dwordx4/x2 loads) and decodes them in registers, part of
-//     them through a 4096-entry window -> value table in LDS and part of them
-//     with ALU arithmetic (the two resources run in parallel);
+//   * each lane reads the code words of 64 consecutive weights of one row
+//     through a buffer descriptor and decodes them in registers, part of them
+//     through an LDS table (window -> value, or for k = 2 a 14-bit pair of
+//     windows -> two codes) and part with ALU arithmetic, so LDS and VALU
+//     work in parallel;
 //   * bf16 MFMA 16x16x32: A = x (rows padded to 16), B = W^T (16 rows);
-//   * tiles shared by several waves are summed in a fixed order through a
-//     small workspace, the last contributor (per-tile counter) writing bf16.
+//   * tiles shared by pieces of one workgroup are summed through LDS, tiles
+//     shared with other workgroups through a workspace, in a fixed order
+//     either way, the last contributor (per-tile counter) writing bf16.
 //
 // Build flags that matter for exactness: -ffp-contract=off.
 
@@ -524,9 +530,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       ++t;
     }
   };
-  // Requests are unconditional (straight-line code keeps the compiler's
-  // memory-counter waits exact); once past the range they repeat its last
-  // unit, which is cache-resident and never decoded again.
+  // Every loop iteration requests the same number of units (straight-line
+  // code keeps the compiler's memory-counter waits exact); the step of the
+  // range's last unit requests nothing, so requests never leave the range.
   auto request = [&](Slot &S) {
     load_words<BITS>(unit_buffer(pt, pb), lane_off, lane_off_next, S.w);
     S.scb = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(pt), lane_off_scale, 0, 0);
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // Prologue. x[:, panel] (M rows and an all-zero row M) is requested
   // first, then the first unit's code words (memory-counter waits are in
   // issue order, so x can be stored to LDS without waiting for the codes);
-  // the window -> value table is built while both are in flight.
+  // the decode table is built while both are in flight.
   const int vecs = panel_k / 8;
   const int xtotal = (pl.m + 1) * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
   {
