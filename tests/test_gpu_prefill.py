@@ -133,18 +133,21 @@ def test_prefill_k_panels_with_whole_tiles_per_wave():
     assert_prefill_close(out[:, rows], y, a, "panels+whole tiles")
 
 
-@pytest.mark.parametrize("bits,shift", [(2, 0), (2, 1), (3, 0), (4, 0)])
-def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift):
+@pytest.mark.parametrize("bits,shift,table", [(2, 0, "pair"), (2, 1, "pair"), (2, 0, "value"), (2, 0, "code"),
+                                              (3, 0, "value"), (3, 0, "code"), (4, 0, "value"), (4, 0, "code")])
+def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift, table, monkeypatch):
     # One-hot x rows pick single columns of W, so every output is one decoded
-    # weight (sum of one exact product): prefill's in-kernel decode (both the
-    # LDS-table and the ALU path) must give exactly the oracle's weights.
-    # Rows hold all 4096 windows; scales cover the 257 reachable values, both
-    # signs, zero, and magnitudes outside 2^-110..2^110 (table-only rows).
-    # For k = 2 the two shifts put the written windows at odd and at even
-    # weight positions: both halves of a pair-table entry.
+    # weight (sum of one exact product): prefill's in-kernel decode (the LDS
+    # table named by `table` and the ALU path) must give exactly the oracle's
+    # weights. Rows hold all 4096 windows; scales cover the 257 reachable
+    # values, both signs, zero, and magnitudes outside 2^-110..2^110 (rows
+    # that take the fallback path). For k = 2 the two shifts put the written
+    # windows at odd and at even weight positions: both halves of a
+    # pair-table entry.
     import torch
 
-    print(f"prefill one-hot exhaustive bits={bits} shift={shift}", flush=True)
+    monkeypatch.setenv("TRELLIS_TABLE", table)
+    print(f"prefill one-hot exhaustive bits={bits} shift={shift} table={table}", flush=True)
     rng = np.random.default_rng(600 + bits + 10 * shift)
     extra = [0x3F80, 0xBF80, 0xBC00, 0xBCA4, 0x0000, 0x8000, 0x0B00, 0x7300, 0x3FFF, 0xC07F,
              0x0600, 0x7900, 0x8600]
@@ -165,6 +168,22 @@ def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift):
         ref = (w_ref[:, cols].T.astype(np.uint32) << 16).view(np.float32)
         bad += int(np.sum(got != ref))  # +0 == -0: zero weights may differ in sign only
     assert bad == 0
+
+
+@pytest.mark.parametrize("bits,table", [(2, "value"), (2, "code"), (2, "pair"), (3, "value"), (3, "code"),
+                                        (4, "value"), (4, "code")])
+@pytest.mark.parametrize("m,k", [(5, 1280), (15, 5120)])
+def test_prefill_each_table(bits, table, m, k, monkeypatch):
+    # Every decode table on one shape with several tiles and a ragged last
+    # tile; M = 15, K = 5120 needs two K panels with the value or pair table
+    # and one with the code table.
+    monkeypatch.setenv("TRELLIS_TABLE", table)
+    n = 84
+    print(f"prefill table={table} m={m} k={k} n={n} bits={bits}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=5000 + 3 * m + bits)
+    out = gpu_prefill(x, codes, scales, bits)
+    y, a = oracle.prefill(x, codes, scales, k, bits)
+    assert_prefill_close(out, y, a, f"table={table} m={m} k={k} bits={bits}")
 
 
 def test_prefill_workspace_grows_between_calls():

@@ -111,33 +111,36 @@ __device__ __forceinline__ uint32_t win12(const uint32_t (&D)[N]) {
   }
 }
 
-// The window times 4: the byte address of its entry in a float table.
-template <int O, int N>
-__device__ __forceinline__ uint32_t win_x4(const uint32_t (&D)[N]) {
+// The window times 2^SH: the byte address of its entry in a table of
+// 2^SH-byte entries (SH = 2: float values, SH = 1: float16 codes).
+template <int O, int SH, int N>
+__device__ __forceinline__ uint32_t win_xa(const uint32_t (&D)[N]) {
   constexpr int w = O >> 5, b = O & 31;
+  constexpr uint32_t m = 0xFFFu << SH;
   static_assert(w < N, "window start outside the lane's words");
-  if constexpr (b >= 2) {
+  if constexpr (b >= SH) {
     if constexpr (b + 12 <= 32) {
-      return (D[w] >> (b - 2)) & 0x3FFCu;
+      return (D[w] >> (b - SH)) & m;
     } else {
       static_assert(w + 1 < N, "straddling window needs the next word");
-      return __builtin_amdgcn_alignbit(D[w + 1], D[w], b - 2) & 0x3FFCu;
+      return __builtin_amdgcn_alignbit(D[w + 1], D[w], b - SH) & m;
     }
   } else {
-    return (D[w] << (2 - b)) & 0x3FFCu;
+    return (D[w] << (SH - b)) & m;
   }
 }
 
-// Table byte addresses (window * 4) of the four windows whose lowest bits
-// are at O0, O0+16, O0+32 and O0+48: two words holding stream bits
-// [O0-2, O0+62) are built once, and each address is one mask of their low or
-// high halves (mask = 0x3FFC in a register, for the SDWA form).
-template <int O0, int N>
-__device__ __forceinline__ void quad_x4(const uint32_t (&D)[N], uint32_t mask, uint32_t (&a)[4]) {
-  constexpr int sh = O0 - 2;
+// Table byte addresses (window * 2^SH) of the four windows whose lowest
+// bits are at O0, O0+16, O0+32 and O0+48: two words holding stream bits
+// [O0-SH, O0-SH+64) are built once, and each address is one mask of their
+// low or high halves (mask = 0xFFF << SH in a register, for the SDWA form).
+template <int O0, int SH, int N>
+__device__ __forceinline__ void quad_xa(const uint32_t (&D)[N], uint32_t mask, uint32_t (&a)[4]) {
+  constexpr int sh = O0 - SH;
+  constexpr uint32_t m = 0xFFFu << SH;
   uint32_t lo, hi;
   if constexpr (sh < 0) {
-    static_assert(sh == -2 || sh == -1, "unexpected window offset");
+    static_assert(sh >= -2, "unexpected window offset");
     lo = D[0] << (-sh);
     hi = __builtin_amdgcn_alignbit(D[1], D[0], 32 + sh);
   } else {
@@ -152,10 +155,18 @@ __device__ __forceinline__ void quad_x4(const uint32_t (&D)[N], uint32_t mask, u
       hi = __builtin_amdgcn_alignbit(D[w + 2], D[w + 1], r);
     }
   }
-  a[0] = lo & 0x3FFCu;
+  a[0] = lo & m;
   a[1] = and_hi16(lo, mask);
-  a[2] = hi & 0x3FFCu;
+  a[2] = hi & m;
   a[3] = and_hi16(hi, mask);
+}
+
+// ---- float16 code table -----------------------------------------------------
+// Entries 2p and 2p + 1 of the 4096-entry window -> code table as one word
+// (every code in [-510, 510] is exact in float16).
+__device__ __forceinline__ uint32_t code_entry_pair(uint32_t p) {
+  const float lo = (float)code_of(2 * p), hi = (float)code_of(2 * p + 1);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 // ---- k = 2 pair table -------------------------------------------------------

@@ -33,6 +33,8 @@
 #include <stdint.h>
 
 #include <map>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -46,14 +48,16 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 16;                 // waves per prefill workgroup (4 per SIMD)
 constexpr int kWgThreads = kWave * kWaves;
-// LDS decode table: window -> float value (4096 entries), or for k = 2
-// 14-bit pair -> two float16 codes (16384 entries).
-constexpr int table_bytes(bool pair) { return pair ? 16384 * 4 : 4096 * 4; }
+// LDS decode tables: window -> float value (4096 x 4 bytes), window ->
+// float16 code (4096 x 2 bytes), or for k = 2 a 14-bit pair of windows ->
+// two float16 codes (16384 x 4 bytes).
+enum TableKind { kValueTable = 0, kCodeTable = 1, kPairTable = 2 };
+constexpr int table_bytes(int tab) { return tab == kPairTable ? 16384 * 4 : tab == kCodeTable ? 4096 * 2 : 4096 * 4; }
 constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
-constexpr int kStageRegs = 9;              // x-staging vectors (16 B) per thread
+constexpr int kStageRegs = 10;             // x-staging vectors (16 B) per thread
 constexpr int kCombineBytes = kWaves * 2 * kWave * 16;  // LDS partial tiles of the end-of-kernel combine
-static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(false), "x staging must cover the largest panel");
+static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(kCodeTable), "x staging must cover the largest panel");
 
 // ---------------------------------------------------------------------------
 // trellis_decode: W[N, K] bf16. One thread per 8 consecutive weights of one
@@ -195,14 +199,28 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t of
   L.d[2 * BITS] = __builtin_amdgcn_raw_buffer_load_b32(r, off_next, 0, 0);
 }
 
-__device__ __forceinline__ float lds_table(const unsigned char *table, uint32_t byte_addr) {
-  return *reinterpret_cast<const float *>(table + byte_addr);
-}
+// A weight from one table entry (byte address a): the value table gives
+// value(window) * s, the code table float32(code * q) -- the same bf16
+// weight for every scale in the ALU path's exact range.
+template <int TAB> struct TableRead;
+template <> struct TableRead<kValueTable> {
+  static constexpr int kShift = 2;  // log2 of the entry size
+  static __device__ __forceinline__ float weight(const unsigned char *table, uint32_t a, float s, float) {
+    return *reinterpret_cast<const float *>(table + a) * s;
+  }
+};
+template <> struct TableRead<kCodeTable> {
+  static constexpr int kShift = 1;
+  static __device__ __forceinline__ float weight(const unsigned char *table, uint32_t a, float, float q) {
+    return mix_lo(*reinterpret_cast<const uint16_t *>(table + a), q);
+  }
+};
 
-template <int BITS, int U, int... S>
+template <int BITS, int TAB, int U, int... S>
 __device__ __forceinline__ bf16x8 group_table(const LaneWords<BITS> &L, const unsigned char *table, float s,
-                                              std::integer_sequence<int, S...>) {
-  const float f[8] = {(lds_table(table, win_x4<(63 - 8 * U - S) * BITS>(L.d)) * s)...};
+                                              float q, std::integer_sequence<int, S...>) {
+  using R = TableRead<TAB>;
+  const float f[8] = {R::weight(table, win_xa<(63 - 8 * U - S) * BITS, R::kShift>(L.d), s, q)...};
   bf16x8 w;
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
@@ -220,12 +238,14 @@ __device__ __forceinline__ bf16x8 group_alu(const LaneWords<BITS> &L, float q, f
 }
 
 // Table-path groups sharing window extraction. Windows 16 bits apart come
-// out of one pair of shifted words (quad_x4): for k = 4 they are 4 weights
+// out of one pair of shifted words (quad_xa): for k = 4 they are 4 weights
 // apart, so groups (U, U+1) share four quads; for k = 2 they are 8 weights
 // apart, so groups U..U+3 share eight quads.
-template <int BITS, int U>
+template <int BITS, int TAB, int U>
 __device__ __forceinline__ void table_span(const LaneWords<BITS> &L, const unsigned char *table, float s,
-                                           uint32_t mask, bf16x8 *w) {
+                                           float q, uint32_t mask, bf16x8 *w) {
+  using R = TableRead<TAB>;
+  constexpr int SH = R::kShift;
   static_assert(BITS == 4 || BITS == 2, "spans exist for k = 4 and k = 2");
   constexpr int G = BITS == 4 ? 2 : 4;  // groups in the span
   constexpr int Q = 8 * G / 4;          // quads in the span
@@ -237,31 +257,31 @@ __device__ __forceinline__ void table_span(const LaneWords<BITS> &L, const unsig
       // idx = 8U + s' + {12, 8, 4, 0}, s' = i (0..3): (group U+1, slot 4+s'),
       // (U+1, s'), (U, 4+s'), (U, s')
       switch (i) {
-        case 0: quad_x4<(63 - (8 * U + 12 + 0)) * 4>(L.d, mask, a); break;
-        case 1: quad_x4<(63 - (8 * U + 12 + 1)) * 4>(L.d, mask, a); break;
-        case 2: quad_x4<(63 - (8 * U + 12 + 2)) * 4>(L.d, mask, a); break;
-        default: quad_x4<(63 - (8 * U + 12 + 3)) * 4>(L.d, mask, a); break;
+        case 0: quad_xa<(63 - (8 * U + 12 + 0)) * 4, SH>(L.d, mask, a); break;
+        case 1: quad_xa<(63 - (8 * U + 12 + 1)) * 4, SH>(L.d, mask, a); break;
+        case 2: quad_xa<(63 - (8 * U + 12 + 2)) * 4, SH>(L.d, mask, a); break;
+        default: quad_xa<(63 - (8 * U + 12 + 3)) * 4, SH>(L.d, mask, a); break;
       }
-      f[1][4 + i] = lds_table(table, a[0]) * s;
-      f[1][i] = lds_table(table, a[1]) * s;
-      f[0][4 + i] = lds_table(table, a[2]) * s;
-      f[0][i] = lds_table(table, a[3]) * s;
+      f[1][4 + i] = R::weight(table, a[0], s, q);
+      f[1][i] = R::weight(table, a[1], s, q);
+      f[0][4 + i] = R::weight(table, a[2], s, q);
+      f[0][i] = R::weight(table, a[3], s, q);
     } else {
       // idx = 8U + s' + {24, 16, 8, 0}, s' = i (0..7): groups U+3, U+2, U+1, U at slot s'
       switch (i) {
-        case 0: quad_x4<(63 - (8 * U + 24 + 0)) * 2>(L.d, mask, a); break;
-        case 1: quad_x4<(63 - (8 * U + 24 + 1)) * 2>(L.d, mask, a); break;
-        case 2: quad_x4<(63 - (8 * U + 24 + 2)) * 2>(L.d, mask, a); break;
-        case 3: quad_x4<(63 - (8 * U + 24 + 3)) * 2>(L.d, mask, a); break;
-        case 4: quad_x4<(63 - (8 * U + 24 + 4)) * 2>(L.d, mask, a); break;
-        case 5: quad_x4<(63 - (8 * U + 24 + 5)) * 2>(L.d, mask, a); break;
-        case 6: quad_x4<(63 - (8 * U + 24 + 6)) * 2>(L.d, mask, a); break;
-        default: quad_x4<(63 - (8 * U + 24 + 7)) * 2>(L.d, mask, a); break;
+        case 0: quad_xa<(63 - (8 * U + 24 + 0)) * 2, SH>(L.d, mask, a); break;
+        case 1: quad_xa<(63 - (8 * U + 24 + 1)) * 2, SH>(L.d, mask, a); break;
+        case 2: quad_xa<(63 - (8 * U + 24 + 2)) * 2, SH>(L.d, mask, a); break;
+        case 3: quad_xa<(63 - (8 * U + 24 + 3)) * 2, SH>(L.d, mask, a); break;
+        case 4: quad_xa<(63 - (8 * U + 24 + 4)) * 2, SH>(L.d, mask, a); break;
+        case 5: quad_xa<(63 - (8 * U + 24 + 5)) * 2, SH>(L.d, mask, a); break;
+        case 6: quad_xa<(63 - (8 * U + 24 + 6)) * 2, SH>(L.d, mask, a); break;
+        default: quad_xa<(63 - (8 * U + 24 + 7)) * 2, SH>(L.d, mask, a); break;
       }
-      f[3][i] = lds_table(table, a[0]) * s;
-      f[2][i] = lds_table(table, a[1]) * s;
-      f[1][i] = lds_table(table, a[2]) * s;
-      f[0][i] = lds_table(table, a[3]) * s;
+      f[3][i] = R::weight(table, a[0], s, q);
+      f[2][i] = R::weight(table, a[1], s, q);
+      f[1][i] = R::weight(table, a[2], s, q);
+      f[0][i] = R::weight(table, a[3], s, q);
     }
   }
 #pragma unroll
@@ -316,8 +336,8 @@ __device__ __forceinline__ void pair_span(const uint32_t (&D)[N], const unsigned
 }
 
 // The pages' arithmetic on the ALU (window, hash, byte sum, reciprocal
-// refinement, scale): the exact fallback of the pair-table kernel for rows
-// whose scale is outside the range where code * q is exact.
+// refinement, scale): the exact fallback of the code- and pair-table kernels
+// for rows whose scale is outside the range where code * q is exact.
 template <int BITS, int U, int... S>
 __device__ __forceinline__ bf16x8 group_exact(const LaneWords<BITS> &L, float s, std::integer_sequence<int, S...>) {
   const float f[8] = {(trellis_value(code_of(win12<(63 - 8 * U - S) * BITS>(L.d))) * s)...};
@@ -327,7 +347,7 @@ __device__ __forceinline__ bf16x8 group_exact(const LaneWords<BITS> &L, float s,
   return w;
 }
 
-template <int BITS, int MASK, bool PAIR, bool EXACT, int U>
+template <int BITS, int MASK, int TAB, bool EXACT, int U>
 __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsigned char *table,
                                            const unsigned char *xa, float s, float q, float k, uint32_t mask,
                                            f32x4 &acc) {
@@ -335,7 +355,7 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
     const bf16x8 w = group_exact<BITS, U>(L, s, std::make_integer_sequence<int, 8>{});
     const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
-  } else if constexpr (PAIR) {
+  } else if constexpr (TAB == kPairTable) {
     static_assert(BITS == 2, "the pair table is for k = 2");
     constexpr bool span = ((MASK >> (U - U % 2)) & 3) == 3;
     if constexpr (span && U % 2 == 0) {
@@ -355,7 +375,7 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
   } else if constexpr (span_start<BITS, MASK, U>()) {
     constexpr int G = BITS == 4 ? 2 : 4;
     bf16x8 w[G];
-    table_span<BITS, U>(L, table, s, mask, w);
+    table_span<BITS, TAB, U>(L, table, s, q, mask, w);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * (U + i));
@@ -364,7 +384,7 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
   } else if constexpr (!in_span<BITS, MASK, U>()) {
     bf16x8 w;
     if constexpr ((MASK >> U) & 1)
-      w = group_table<BITS, U>(L, table, s, std::make_integer_sequence<int, 8>{});
+      w = group_table<BITS, TAB, U>(L, table, s, q, std::make_integer_sequence<int, 8>{});
     else
       w = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
     const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xa + 16 * U);
@@ -372,11 +392,11 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
   }
 }
 
-template <int BITS, int MASK, bool PAIR, bool EXACT, int... U>
+template <int BITS, int MASK, int TAB, bool EXACT, int... U>
 __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned char *table, const unsigned char *xa,
                                      float s, float q, float k, uint32_t mask, f32x4 &acc,
                                      std::integer_sequence<int, U...>) {
-  (unit_group<BITS, MASK, PAIR, EXACT, U>(L, table, xa, s, q, k, mask, acc), ...);
+  (unit_group<BITS, MASK, TAB, EXACT, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
 __device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
@@ -444,7 +464,7 @@ __device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int til
   return sum;
 }
 
-template <int BITS, int MASK, bool PAIR>
+template <int BITS, int MASK, int TAB>
 __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__restrict__ x,
                                                              const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
@@ -455,7 +475,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
   // After the main loop the x region is reused for the waves' partial tiles.
-  __shared__ __attribute__((aligned(16))) uint32_t s_table[table_bytes(PAIR) / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_table[table_bytes(TAB) / 4];
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
   unsigned char *const xl = lds;
@@ -538,26 +558,27 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     S.scb = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(pt), lane_off_scale, 0, 0);
     if (++pu < u1) advance(pt, pb);
   };
-  // Prologue. x[:, panel] (M rows and an all-zero row M) is requested
-  // first, then the first unit's code words (memory-counter waits are in
+  // Prologue. x[:, panel] (M rows) is requested first, then the first unit's code words (memory-counter waits are in
   // issue order, so x can be stored to LDS without waiting for the codes);
   // the decode table is built while both are in flight.
   const int vecs = panel_k / 8;
-  const int xtotal = (pl.m + 1) * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
+  const int xtotal = pl.m * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
   {
     uint4 xv[kStageRegs];
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
       const int idx = r * kWgThreads + tid;
-      xv[r] = uint4{0u, 0u, 0u, 0u};
+      xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
       if (idx < xtotal) {
         const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
-        if (i < pl.m) xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
+        xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
       }
     }
     request(S0);
-    if constexpr (PAIR) {
+    if constexpr (TAB == kPairTable) {
       for (int e = tid; e < 16384; e += kWgThreads) s_table[e] = pair_entry((uint32_t)e);
+    } else if constexpr (TAB == kCodeTable) {
+      for (int e = tid; e < 2048; e += kWgThreads) s_table[e] = code_entry_pair((uint32_t)e);
     } else {
       for (int e = tid; e < 4096; e += kWgThreads)
         s_table[e] = __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)e)));
@@ -574,7 +595,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
 
   __syncthreads();
 
-  const unsigned char *xa = xl + (j < pl.m ? j : pl.m) * pl.x_stride + (192 - 64 * g) * 2;
+  // A-operand rows j >= M read row M - 1: they only feed output rows >= M,
+  // which are never stored.
+  const unsigned char *xa = xl + (j < pl.m ? j : pl.m - 1) * pl.x_stride + (192 - 64 * g) * 2;
 
   // Tiles of this wave's range: a cross tile's partial is staged in the
   // workspace as soon as its units here are done (its counter is bumped after
@@ -603,8 +626,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float s = scale_of(S0.scb), q, kq;
     alu_row_constants(s, q, kq);
-    bool table_only = !__all(alu_scale_ok(s));
-    const uint32_t mask_addr = PAIR ? 0xFFFCu : 0x3FFCu;  // table byte-address mask (SDWA operand)
+    bool out_of_range = !__all(alu_scale_ok(s));
+    // table byte-address mask (SDWA operand)
+    const uint32_t mask_addr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
     int u = u0;
     // Decode unit u from slot C while unit u + 1 is requested into slot N;
     // the range's last unit requests nothing (`last`), so no load is left in
@@ -616,16 +640,18 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
         s = scale_of(C.scb);
         alu_row_constants(s, q, kq);
-        table_only = !__all(alu_scale_ok(s));
+        out_of_range = !__all(alu_scale_ok(s));
       }
       if constexpr (!decltype(last)::value) request(N);
       const unsigned char *xb = xa + b * 512;
       // Rows whose scale is outside the exact range of code * q: the value
-      // table (or, with the pair table, the ALU chain) for every group.
-      if (table_only)
-        unit<BITS, 0xFF, false, PAIR>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
+      // table (with the code or pair table, the pages' chain on the ALU) for
+      // every group.
+      if (out_of_range)
+        unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(C.w, table, xb, s, q, kq, mask_addr, acc,
+                                                          std::make_integer_sequence<int, 8>{});
       else
-        unit<BITS, MASK, PAIR, false>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, MASK, TAB, false>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
       advance(tile, b);
       ++u;
       // A SIMD issues from its highest-priority ready wave, oldest first
@@ -796,7 +822,7 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   for (int p = 1; p <= kb; ++p) {
     if (kb % p) continue;
     const int stride = (kb / p) * 512 + 16;
-    if (table + (m + 1) * stride <= kMaxLds) {
+    if (table + m * stride <= kMaxLds) {
       panels = p;
       break;
     }
@@ -823,18 +849,21 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   pl.maxc = (pl.kp - 1) / (pl.cq / s_min) + 2;
   // Dynamic LDS: the x panel, later reused for the pieces' partial tiles
   // (two 16x16 fp32 tiles per wave); the static table adds `table` bytes.
-  int need = (m + 1) * pl.x_stride;
+  int need = m * pl.x_stride;
   if (need < kCombineBytes) need = kCombineBytes;
   pl.lds_bytes = need + table > kMinLds ? need : kMinLds - table;
   return pl;
 }
 
-// Prefill kernels: k = 2 (value table), 3, 4, and k = 2 with the pair table.
-enum Variant { kK2 = 0, kK3 = 1, kK4 = 2, kK2Pair = 3, kVariants = 4 };
+// Prefill kernels: k = 2, 3, 4 with the value or the code table, and k = 2
+// with the pair table. Variant = 2 * (k - 2) + table kind, pair = 6.
+enum Variant { kVariantPair = 6, kVariants = 7 };
+constexpr int variant_of(int bits, int tab) { return tab == kPairTable ? kVariantPair : 2 * (bits - 2) + tab; }
+constexpr int variant_table(int v) { return v == kVariantPair ? kPairTable : v % 2; }
 
 struct DeviceState {
   int cus = 0;
-  bool lds_attr_set[kVariants] = {false, false, false, false};
+  bool lds_attr_set[kVariants] = {};
 };
 
 struct Workspace {
@@ -850,16 +879,21 @@ std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-const void *prefill_fn(Variant v) {
+typedef void (*PrefillFn)(const uint16_t *, const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *,
+                          uint16_t *, float *, uint32_t *, Plan);
+PrefillFn prefill_fn(int v) {
   switch (v) {
-    case kK2: return reinterpret_cast<const void *>(&prefill_kernel<2, Mix<2>::kMask, false>);
-    case kK3: return reinterpret_cast<const void *>(&prefill_kernel<3, Mix<3>::kMask, false>);
-    case kK4: return reinterpret_cast<const void *>(&prefill_kernel<4, Mix<4>::kMask, false>);
-    default: return reinterpret_cast<const void *>(&prefill_kernel<2, Mix<2, true>::kMask, true>);
+    case 0: return &prefill_kernel<2, Mix<2>::kMask, kValueTable>;
+    case 1: return &prefill_kernel<2, Mix<2>::kMask, kCodeTable>;
+    case 2: return &prefill_kernel<3, Mix<3>::kMask, kValueTable>;
+    case 3: return &prefill_kernel<3, Mix<3>::kMask, kCodeTable>;
+    case 4: return &prefill_kernel<4, Mix<4>::kMask, kValueTable>;
+    case 5: return &prefill_kernel<4, Mix<4>::kMask, kCodeTable>;
+    default: return &prefill_kernel<2, Mix<2, true>::kMask, kPairTable>;
   }
 }
 
-trellis_status device_state(DeviceState *&st, Variant v) {
+trellis_status device_state(DeviceState *&st, int v) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
   DeviceState &d = g_dev[dev];
@@ -868,8 +902,8 @@ trellis_status device_state(DeviceState *&st, Variant v) {
       return TRELLIS_E_HIP;
   }
   if (!d.lds_attr_set[v]) {
-    if (hipFuncSetAttribute(prefill_fn(v), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kMaxLds - table_bytes(v == kK2Pair)) != hipSuccess)
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_fn(v)), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLds - table_bytes(variant_table(v))) != hipSuccess)
       return TRELLIS_E_HIP;
     d.lds_attr_set[v] = true;
   }
@@ -959,10 +993,21 @@ trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16
 namespace trellis {
 namespace {
 
-// The fused layer for any 1 <= m <= 15 with a valid geometry (rows of A past
-// m are zero in LDS); the entry points restrict m to their regimes. With a
-// second matrix (codes2, scales2), both projections go through one launch
-// into the gate/up scratch and gate_up_kernel writes out = silu(gate) * up.
+// TRELLIS_TABLE=value|code|pair in the environment forces the decode table
+// (testing and tuning); pair applies to k = 2 only. -1: no override.
+int table_override(int bits) {
+  const char *e = std::getenv("TRELLIS_TABLE");
+  if (!e) return -1;
+  if (!std::strcmp(e, "value")) return kValueTable;
+  if (!std::strcmp(e, "code")) return kCodeTable;
+  if (!std::strcmp(e, "pair") && bits == 2) return kPairTable;
+  return -1;
+}
+
+// The fused layer for any 1 <= m <= 15 with a valid geometry; the entry
+// points restrict m to their regimes. With a second matrix (codes2,
+// scales2), both projections go through one launch into the gate/up scratch
+// and gate_up_kernel writes out = silu(gate) * up.
 trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
                              const uint16_t *scales_bf16, const uint32_t *codes2, const uint16_t *scales2,
                              trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
@@ -976,21 +1021,33 @@ trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *
   int cus = 0;
   {
     DeviceState *st0 = nullptr;
-    const trellis_status rc0 = device_state(st0, g.bits == 3 ? kK3 : g.bits == 4 ? kK4 : kK2);
+    const trellis_status rc0 = device_state(st0, variant_of(g.bits, kValueTable));
     if (rc0 != TRELLIS_OK) return rc0;
     cus = st0->cus;
   }
-  // k = 2 uses the pair table unless its larger footprint would split x
-  // into more K panels than the value table does.
-  Variant v = g.bits == 3 ? kK3 : g.bits == 4 ? kK4 : kK2;
-  Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(false), two);
-  if (v == kK2) {
-    const Plan pp = make_plan(m, g.n, g.k, cus, table_bytes(true), two);
-    if (pp.panels == pl.panels) {
-      pl = pp;
-      v = kK2Pair;
+  // The table that splits x into the fewest K panels; among equals the pair
+  // table (k = 2), then the value table. TRELLIS_TABLE overrides the choice.
+  int tab = kValueTable;
+  Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(kValueTable), two);
+  const int forced = table_override(g.bits);
+  if (forced >= 0) {
+    tab = forced;
+    pl = make_plan(m, g.n, g.k, cus, table_bytes(tab), two);
+  } else {
+    const Plan pc = make_plan(m, g.n, g.k, cus, table_bytes(kCodeTable), two);
+    if (pc.panels < pl.panels) {
+      pl = pc;
+      tab = kCodeTable;
+    }
+    if (g.bits == 2) {
+      const Plan pp = make_plan(m, g.n, g.k, cus, table_bytes(kPairTable), two);
+      if (pp.panels <= pl.panels) {
+        pl = pp;
+        tab = kPairTable;
+      }
     }
   }
+  const int v = variant_of(g.bits, tab);
   DeviceState *st = nullptr;
   trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
@@ -1005,24 +1062,8 @@ trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *
   }
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
-  switch (v) {
-    case kK2:
-      hipLaunchKernelGGL((prefill_kernel<2, Mix<2>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
-      break;
-    case kK3:
-      hipLaunchKernelGGL((prefill_kernel<3, Mix<3>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
-      break;
-    case kK4:
-      hipLaunchKernelGGL((prefill_kernel<4, Mix<4>::kMask, false>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
-      break;
-    default:
-      hipLaunchKernelGGL((prefill_kernel<2, Mix<2, true>::kMask, true>), grid, block, pl.lds_bytes, stream, x_bf16,
-                         codes, scales_bf16, codes2, scales2, dst, w->ws, w->counters, pl);
-      break;
-  }
+  hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, x_bf16, codes, scales_bf16, codes2, scales2,
+                     dst, w->ws, w->counters, pl);
   if (two) {
     const int64_t total = (int64_t)m * g.n;
     hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
