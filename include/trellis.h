@@ -52,6 +52,12 @@
  * ordered by the stream. Host-side state is guarded by a mutex, so calls
  * may come from several threads. Errors are returned, never thrown; a
  * validation error leaves every output untouched.
+ *
+ * Decode table: the library picks, per call, the LDS table that lets the
+ * most of x stay in one K panel (a window -> value table, a window ->
+ * float16 code table, or for k = 2 a table of code pairs). The environment
+ * variable TRELLIS_TABLE = value | code | pair forces one (for testing and
+ * tuning; pair only for k = 2); every table gives the same weights.
  */
 #ifndef TRELLIS_H
 #define TRELLIS_H
@@ -69,6 +75,8 @@ extern "C" {
 #define TRELLIS_MATVEC_MAX_M 4
 #define TRELLIS_MAX_K (1 << 18)
 #define TRELLIS_MAX_N (1 << 22)
+#define TRELLIS_MAX_GROUPS 4096
+#define TRELLIS_MAX_GROUP_ROWS (1 << 20)
 
 /* Geometry of one packed linear layer: n output rows (out features), k input
  * columns (in features), block length t (must be 256), window length l (must
@@ -84,7 +92,7 @@ typedef struct trellis_geom {
 typedef enum trellis_status {
     TRELLIS_OK = 0,
     TRELLIS_E_GEOMETRY = -1, /* t, l, bits, n or k outside the accepted domain */
-    TRELLIS_E_M = -2,        /* m outside [5, 15] (prefill) or [1, 4] (matvec) */
+    TRELLIS_E_M = -2,        /* m outside [5, 15] (prefill) or [1, 4] (matvec); bad packed group or row counts */
     TRELLIS_E_NULL = -3,     /* a required pointer is NULL */
     TRELLIS_E_ALIGN = -4,    /* a pointer is not aligned as documented */
     TRELLIS_E_HIP = -5       /* the HIP runtime reported a launch error */
@@ -123,6 +131,30 @@ trellis_status trellis_prefill(const uint16_t *x_bf16, int32_t m,
 trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m,
                               const uint32_t *codes, const uint16_t *scales_bf16,
                               trellis_geom g, uint16_t *out_bf16, void *hip_stream);
+
+/* Token packing: the rows of several independent inputs go through the
+ * layer together, so one decode of W serves all of them (page "mlx-bun
+ * 0.4.0 -> 0.5.0" (npm diff, page 26), section src/model/token-groups.ts:
+ * the tokenwise operation runs on the concatenation of the groups' rows and
+ * the result is cut back into each group's shape; section
+ * src/model/qwen3_5.ts, mixed forward pass, applies it to the MLP).
+ *   x_groups[i]   bf16 [rows[i], K], row-major, 16-byte aligned
+ *   out_groups[i] bf16 [rows[i], N], row-major, 16-byte aligned
+ * for 0 <= i < groups (1 <= groups <= TRELLIS_MAX_GROUPS; 0 <= rows[i] <=
+ * TRELLIS_MAX_GROUP_ROWS; a group with no rows may pass NULL pointers; at
+ * least one row in total). The packed rows, in group order, are processed
+ * in launches of at most TRELLIS_MAX_M rows (the wide kernel's limit; the
+ * page's concatenation has no limit of its own), and no concatenated copy
+ * of x or out is made: the kernel reads x rows and writes output rows
+ * through per-row pointers. Each output row meets trellis_prefill's
+ * tolerance; the summation order, and so the last bit, may differ from an
+ * unpacked call. Same formats, codes and scales as trellis_prefill.
+ * Validation errors (TRELLIS_E_M for bad group or row counts) are found
+ * before any launch; a launch error stops the call with earlier launches
+ * already enqueued. */
+trellis_status trellis_prefill_packed(const uint16_t *const *x_groups, const int32_t *rows, int32_t groups,
+                                      const uint32_t *codes, const uint16_t *scales_bf16, trellis_geom g,
+                                      uint16_t *const *out_groups, void *hip_stream);
 
 /* The MLP's gate and up projections of one x, fused:
  *   h[M, N] = bf16(bf16(gate * bf16(sigmoid(gate))) * up),

@@ -163,3 +163,40 @@ def test_gate_up_rejects_before_launch(lib):
     assert call_gate_up(m=0, x=None) == tp.E_M
     with pytest.raises(ValueError):
         tp.gate_up_raw(FAKE, 16, FAKE, FAKE, FAKE, FAKE, tp.geom(**GOOD), FAKE, 0)
+
+
+def call_packed(xs=(FAKE, FAKE), rows=(2, 3), cd=FAKE, sc=FAKE, g=None, outs=(FAKE, FAKE), groups=None):
+    import ctypes
+
+    g = g or tp.geom(**GOOD)
+    lib = tp.load_library()
+    n = len(rows) if rows is not None else 2
+    xa = None if xs is None else (ctypes.c_void_p * max(n, 1))(*xs)
+    ra = None if rows is None else (ctypes.c_int32 * max(n, 1))(*rows)
+    oa = None if outs is None else (ctypes.c_void_p * max(n, 1))(*outs)
+    return lib.trellis_prefill_packed(xa, ra, n if groups is None else groups, cd, sc, g, oa, None)
+
+
+def test_prefill_packed_rejects_before_launch(lib):
+    assert call_packed(g=tp.geom(17408, 5000, 4)) == tp.E_GEOMETRY
+    assert call_packed(xs=None) == tp.E_NULL
+    assert call_packed(rows=None, groups=2) == tp.E_NULL
+    assert call_packed(outs=None) == tp.E_NULL
+    assert call_packed(cd=None) == tp.E_NULL
+    assert call_packed(sc=None) == tp.E_NULL
+    assert call_packed(groups=0) == tp.E_M
+    assert call_packed(groups=tp.MAX_GROUPS + 1) == tp.E_M
+    assert call_packed(rows=(2, -1)) == tp.E_M
+    assert call_packed(rows=(0, 0)) == tp.E_M
+    assert call_packed(rows=(2, tp.MAX_GROUP_ROWS + 1)) == tp.E_M
+    assert call_packed(xs=(FAKE, None)) == tp.E_NULL
+    assert call_packed(outs=(None, FAKE)) == tp.E_NULL
+    assert call_packed(xs=(FAKE, FAKE + 2)) == tp.E_ALIGN
+    assert call_packed(outs=(FAKE + 8, FAKE)) == tp.E_ALIGN
+    assert call_packed(cd=FAKE + 4) == tp.E_ALIGN
+    assert call_packed(sc=FAKE + 1) == tp.E_ALIGN
+    # groups with no rows may pass NULL pointers; geometry is checked first
+    assert call_packed(xs=(None, FAKE + 2), rows=(0, 3)) == tp.E_ALIGN
+    assert call_packed(g=tp.geom(17408, 5000, 4), xs=None) == tp.E_GEOMETRY
+    with pytest.raises(ValueError):
+        tp.prefill_packed_raw([FAKE], [0], FAKE, FAKE, tp.geom(**GOOD), [FAKE], 0)

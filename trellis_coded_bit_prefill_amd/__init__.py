@@ -24,6 +24,8 @@ L_WINDOW = 12
 MIN_M = 5
 MAX_M = 15
 MATVEC_MAX_M = 4
+MAX_GROUPS = 4096
+MAX_GROUP_ROWS = 1 << 20
 
 OK = 0
 E_GEOMETRY = -1
@@ -33,8 +35,8 @@ E_ALIGN = -4
 E_HIP = -5
 
 # Every symbol declared in include/trellis.h.
-EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_gate_up",
-            "trellis_status_string")
+EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_prefill_packed",
+            "trellis_gate_up", "trellis_status_string")
 
 
 class Geom(ctypes.Structure):
@@ -80,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_prefill.restype = ctypes.c_int
     L.trellis_matvec.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
     L.trellis_matvec.restype = ctypes.c_int
+    L.trellis_prefill_packed.argtypes = [vp, vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
+    L.trellis_prefill_packed.restype = ctypes.c_int
     L.trellis_gate_up.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, Geom, vp, vp]
     L.trellis_gate_up.restype = ctypes.c_int
     _lib = L
@@ -148,6 +152,18 @@ def matvec_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out
                stream: int) -> None:
     """Direct C-ABI call with raw device addresses (1 <= m <= 4)."""
     _raise(load_library().trellis_matvec(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
+
+
+def prefill_packed_raw(x_ptrs, rows, codes_ptr: int, scales_ptr: int, g: Geom, out_ptrs, stream: int) -> None:
+    """Direct C-ABI call: x_ptrs, rows and out_ptrs are equal-length
+    sequences of raw device addresses and row counts, one per group."""
+    groups = len(rows)
+    if len(x_ptrs) != groups or len(out_ptrs) != groups:
+        raise ValueError("x_ptrs, rows and out_ptrs must have one entry per group")
+    xa = (ctypes.c_void_p * max(groups, 1))(*x_ptrs)
+    ra = (ctypes.c_int32 * max(groups, 1))(*rows)
+    oa = (ctypes.c_void_p * max(groups, 1))(*out_ptrs)
+    _raise(load_library().trellis_prefill_packed(xa, ra, groups, codes_ptr, scales_ptr, g, oa, stream))
 
 
 def gate_up_raw(x_ptr: int, m: int, codes_gate_ptr: int, scales_gate_ptr: int, codes_up_ptr: int,
@@ -226,6 +242,43 @@ def _linear(entry, x, codes, scales, bits: int, out=None):
     entry(x.data_ptr(), m, codes.data_ptr(), scales.data_ptr(), geom(n, k, bits), out.data_ptr(),
           _stream_handle(x.device))
     return out
+
+
+def prefill_packed(xs, codes, scales, bits: int, outs=None):
+    """Token packing: one pass of the layer over the rows of every x in xs
+    (each [rows_i, K], any rows_i >= 0), outputs cut back per input
+    ([rows_i, N] each). Rows are processed in launches of at most 15."""
+    import torch
+
+    bf, cw = _dtypes()
+    if len(xs) == 0:
+        raise ValueError("xs must hold at least one input")
+    _check_tensor("codes", codes, cw, 2)
+    _check_tensor("scales", scales, bf, 1, codes.device)
+    n = codes.shape[0]
+    if scales.shape[0] != n:
+        raise ValueError("scales must have one entry per row")
+    k = None
+    for i, x in enumerate(xs):
+        _check_tensor(f"xs[{i}]", x, bf, 2, codes.device)
+        if k is None:
+            k = x.shape[1]
+        elif x.shape[1] != k:
+            raise ValueError("every input must have the same K")
+    if codes.shape[1] * 32 != k * bits:
+        raise ValueError(f"codes has {codes.shape[1]} words per row, expected K*bits/32 = {k * bits // 32}")
+    if outs is None:
+        outs = [torch.empty((x.shape[0], n), dtype=torch.bfloat16, device=codes.device) for x in xs]
+    if len(outs) != len(xs):
+        raise ValueError("outs must have one tensor per input")
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        _check_tensor(f"outs[{i}]", o, bf, 2, codes.device)
+        if tuple(o.shape) != (x.shape[0], n):
+            raise ValueError(f"outs[{i}] must be [{x.shape[0]}, {n}]")
+    prefill_packed_raw([x.data_ptr() if x.shape[0] else 0 for x in xs], [x.shape[0] for x in xs],
+                       codes.data_ptr(), scales.data_ptr(), geom(n, k, bits),
+                       [o.data_ptr() if o.shape[0] else 0 for o in outs], _stream_handle(codes.device))
+    return outs
 
 
 def gate_up(x, codes_gate, scales_gate, codes_up, scales_up, bits: int, out=None):

@@ -46,6 +46,8 @@ namespace trellis {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kMaxRows = 16;               // row-pointer slots (m <= 15)
+constexpr int kRowTableBytes = kMaxRows * 8;  // LDS copy of the output row pointers
 constexpr int kWaves = 16;                 // waves per prefill workgroup (4 per SIMD)
 constexpr int kWgThreads = kWave * kWaves;
 // LDS decode tables: window -> float value (4096 x 4 bytes), window ->
@@ -95,12 +97,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
 // trellis_prefill
 // ---------------------------------------------------------------------------
 
+// Rows of x and of the output, one pointer each: row i of x is
+// x[i][0 .. K), row i of the output out[i][0 .. out_rows). Rows of one
+// array are consecutive for a plain call; packed calls gather rows of
+// several arrays. Entries past m are unused.
+struct RowPtrs {
+  const uint16_t *x[kMaxRows];
+  uint16_t *out[kMaxRows];
+};
+
 // Work partition, computed on the host and re-derived by every wave.
 struct Plan {
   int32_t m, n, k;
   int32_t tiles;     // ceil(N / 16), or twice that for two matrices
   int32_t half;      // two matrices: tiles of the first (the second's start); 0 for one
-  int32_t out_rows;  // columns of out (its row stride): N, or 32 * half for two matrices
+  int32_t out_rows;  // columns of an output row: N, or 32 * half for two matrices
   int32_t panels;    // K panels (x panel staged per workgroup)
   int32_t kp;        // 256-weight blocks per panel
   int32_t groups;    // workgroups per panel
@@ -111,6 +122,7 @@ struct Plan {
   int32_t cq;        // units / groups: every workgroup gets cq or cq + 1 units
   int32_t cr;        // units % groups: the first cr workgroups get cq + 1
   uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
+  int32_t x_contiguous;  // 1: x row i is at row 0 + i * K (plain calls); 0: per-row pointers
 };
 
 // Split of a workgroup's contiguous units [u0, u0 + len) into s <= 16
@@ -399,12 +411,14 @@ __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned ch
   (unit_group<BITS, MASK, TAB, EXACT, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
-__device__ __forceinline__ void store_tile(uint16_t *__restrict__ out, f32x4 v, int m, int n, int row, int g) {
-  if (row >= n) return;
-  const uint32_t off = (uint32_t)(4 * g) * (uint32_t)n + (uint32_t)row;
+// Lane (j, g) holds rows 4g .. 4g+3 of output column `col`; the row
+// pointers come from the LDS copy of the row table.
+__device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, int m, int ncols, int col, int g) {
+  if (col >= ncols) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (4 * g + e < m) out[off + (uint32_t)(e * n)] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+    if (4 * g + e < m)
+      reinterpret_cast<uint16_t *>(rows[4 * g + e])[col] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
 }
 
 // Partials of tiles shared with other workgroups go through the workspace:
@@ -465,17 +479,17 @@ __device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int til
 }
 
 template <int BITS, int MASK, int TAB>
-__global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__restrict__ x,
-                                                             const uint32_t *__restrict__ codes,
+__global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
                                                              const uint32_t *__restrict__ codes2,
                                                              const uint16_t *__restrict__ scales2,
-                                                             uint16_t *__restrict__ out, float *__restrict__ ws,
-                                                             uint32_t *__restrict__ counters, Plan pl) {
+                                                             float *__restrict__ ws, uint32_t *__restrict__ counters,
+                                                             Plan pl, RowPtrs rp) {
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
   // After the main loop the x region is reused for the waves' partial tiles.
   __shared__ __attribute__((aligned(16))) uint32_t s_table[table_bytes(TAB) / 4];
+  __shared__ uint64_t s_rows[kMaxRows];  // output row pointers
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char *const table = reinterpret_cast<unsigned char *>(s_table);
   unsigned char *const xl = lds;
@@ -569,10 +583,29 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     for (int r = 0; r < kStageRegs; ++r) {
       const int idx = r * kWgThreads + tid;
       xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
-      if (idx < xtotal) {
-        const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
-        xv[r] = *reinterpret_cast<const uint4 *>(x + (int64_t)i * pl.k + kbase + 8 * c);
+      if (pl.x_contiguous) {
+        // Rows K elements apart from row 0: one base address.
+        if (idx < xtotal) {
+          const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
+          xv[r] = *reinterpret_cast<const uint4 *>(rp.x[0] + (int64_t)i * pl.k + kbase + 8 * c);
+        }
+      } else {
+        // A wave's 64 vectors start at a multiple of 64 and a row holds a
+        // multiple of 32 of them, so they lie in rows i0 and i0 + 1 (uniform).
+        const int i0 = min((int)__umulhi((uint32_t)(r * kWgThreads + wave * kWave), pl.xdiv), kMaxRows - 2);
+        const uint16_t *const x0 = rp.x[i0], *const x1 = rp.x[i0 + 1];
+        if (idx < xtotal) {
+          const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
+          xv[r] = *reinterpret_cast<const uint4 *>((i == i0 ? x0 : x1) + kbase + 8 * c);
+        }
       }
+    }
+    if (wave == 0) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int r = 0; r < kMaxRows; ++r)
+        if (lane == r) v = reinterpret_cast<uint64_t>(rp.out[r]);
+      if (lane < kMaxRows) s_rows[lane] = v;
     }
     request(S0);
     if constexpr (TAB == kPairTable) {
@@ -619,7 +652,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
   auto tile_done = [&](int t, f32x4 v) {
     if (cross(t)) stage(t, v);
     else if (t == tf && u0 > t * pl.kp) part_f = v;
-    else store_tile(out, v, pl.m, pl.out_rows, t * 16 + j, g);
+    else store_tile(s_rows, v, pl.m, pl.out_rows, t * 16 + j, g);
   };
   if (active) {
     int cur = tile;
@@ -678,7 +711,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
     }
     tl = cur;
     if (cross(cur)) stage(cur, acc);
-    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(out, acc, pl.m, pl.out_rows, cur * 16 + j, g);
+    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(s_rows, acc, pl.m, pl.out_rows, cur * 16 + j, g);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
@@ -707,7 +740,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
         last &= last - 1;
         const int T = t0 + i;
         const int c = __shfl(contrib, i);
-        store_tile(out, sum_partials(pl, ws, T, c, lane), pl.m, pl.out_rows, T * 16 + j, g);
+        store_tile(s_rows, sum_partials(pl, ws, T, c, lane), pl.m, pl.out_rows, T * 16 + j, g);
         if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -752,7 +785,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint16_t *__r
       for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
       if (e >= t1u) break;  // T ends in this segment
     }
-    store_tile(out, sum, pl.m, pl.out_rows, T * 16 + j, g);
+    store_tile(s_rows, sum, pl.m, pl.out_rows, T * 16 + j, g);
   }
 }
 
@@ -822,7 +855,7 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   for (int p = 1; p <= kb; ++p) {
     if (kb % p) continue;
     const int stride = (kb / p) * 512 + 16;
-    if (table + m * stride <= kMaxLds) {
+    if (table + kRowTableBytes + m * stride <= kMaxLds) {
       panels = p;
       break;
     }
@@ -848,10 +881,11 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   const int s_min = pl.cq < kWaves ? pl.cq : kWaves;
   pl.maxc = (pl.kp - 1) / (pl.cq / s_min) + 2;
   // Dynamic LDS: the x panel, later reused for the pieces' partial tiles
-  // (two 16x16 fp32 tiles per wave); the static table adds `table` bytes.
+  // (two 16x16 fp32 tiles per wave).
   int need = m * pl.x_stride;
   if (need < kCombineBytes) need = kCombineBytes;
-  pl.lds_bytes = need + table > kMinLds ? need : kMinLds - table;
+  const int fixed = table + kRowTableBytes;  // static LDS: decode table and row table
+  pl.lds_bytes = need + fixed > kMinLds ? need : kMinLds - fixed;
   return pl;
 }
 
@@ -879,8 +913,8 @@ std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-typedef void (*PrefillFn)(const uint16_t *, const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *,
-                          uint16_t *, float *, uint32_t *, Plan);
+typedef void (*PrefillFn)(const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *, float *, uint32_t *,
+                          Plan, RowPtrs);
 PrefillFn prefill_fn(int v) {
   switch (v) {
     case 0: return &prefill_kernel<2, Mix<2>::kMask, kValueTable>;
@@ -903,7 +937,7 @@ trellis_status device_state(DeviceState *&st, int v) {
   }
   if (!d.lds_attr_set[v]) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_fn(v)), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kMaxLds - table_bytes(variant_table(v))) != hipSuccess)
+                            kMaxLds - table_bytes(variant_table(v)) - kRowTableBytes) != hipSuccess)
       return TRELLIS_E_HIP;
     d.lds_attr_set[v] = true;
   }
@@ -1004,20 +1038,16 @@ int table_override(int bits) {
   return -1;
 }
 
-// The fused layer for any 1 <= m <= 15 with a valid geometry; the entry
-// points restrict m to their regimes. With a second matrix (codes2,
-// scales2), both projections go through one launch into the gate/up scratch
-// and gate_up_kernel writes out = silu(gate) * up.
-trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
-                             const uint16_t *scales_bf16, const uint32_t *codes2, const uint16_t *scales2,
-                             trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
-  const bool two = codes2 != nullptr || scales2 != nullptr;
-  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16 || (two && (!codes2 || !scales2))) return TRELLIS_E_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
-    return TRELLIS_E_ALIGN;
-  if (two && (!aligned(codes2, 16) || !aligned(scales2, 2))) return TRELLIS_E_ALIGN;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  std::lock_guard<std::mutex> lock(g_mu);
+// One launch of the layer on m <= 15 rows (any m >= 1 with a valid
+// geometry; the entry points restrict m to their regimes): x row i at
+// x_rows[i], output row i at out_rows[i]. With a second matrix (codes2,
+// scales2) both projections go to the gate/up scratch in the same launch,
+// and gate_up_kernel then writes silu(gate) * up to the [m, N] array at
+// out_rows[0] (rows consecutive).
+trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_rows, int32_t m,
+                           const uint32_t *codes, const uint16_t *scales_bf16, const uint32_t *codes2,
+                           const uint16_t *scales2, trellis_geom g, hipStream_t stream) {
+  const bool two = codes2 != nullptr;
   int cus = 0;
   {
     DeviceState *st0 = nullptr;
@@ -1054,22 +1084,54 @@ trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *
   Workspace *w = nullptr;
   rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256, (size_t)pl.tiles, w);
   if (rc != TRELLIS_OK) return rc;
-  uint16_t *dst = out_bf16;
+  RowPtrs rp{};
+  pl.x_contiguous = 1;
+  for (int i = 0; i < m; ++i) {
+    rp.x[i] = x_rows[i];
+    if (x_rows[i] != x_rows[0] + (size_t)i * g.k) pl.x_contiguous = 0;
+  }
   if (two) {
     rc = gate_up_scratch(*w, (size_t)m * pl.out_rows);
     if (rc != TRELLIS_OK) return rc;
-    dst = w->gu;
+    for (int i = 0; i < m; ++i) rp.out[i] = w->gu + (size_t)i * pl.out_rows;
+  } else {
+    for (int i = 0; i < m; ++i) rp.out[i] = out_rows[i];
+  }
+  // Unused slots repeat row 0 (never dereferenced).
+  for (int i = m; i < kMaxRows; ++i) {
+    rp.x[i] = rp.x[0];
+    rp.out[i] = rp.out[0];
   }
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
-  hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, x_bf16, codes, scales_bf16, codes2, scales2,
-                     dst, w->ws, w->counters, pl);
+  hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, codes, scales_bf16, codes2, scales2, w->ws,
+                     w->counters, pl, rp);
   if (two) {
     const int64_t total = (int64_t)m * g.n;
     hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       (const uint16_t *)dst, m, g.n, pl.half * 16, out_bf16);
+                       (const uint16_t *)w->gu, m, g.n, pl.half * 16, out_rows[0]);
   }
   return launch_status();
+}
+
+// Plain calls: x [m, K] and out [m, N], rows consecutive.
+trellis_status launch_linear(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                             const uint16_t *scales_bf16, const uint32_t *codes2, const uint16_t *scales2,
+                             trellis_geom g, uint16_t *out_bf16, void *hip_stream) {
+  const bool two = codes2 != nullptr || scales2 != nullptr;
+  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16 || (two && (!codes2 || !scales2))) return TRELLIS_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
+    return TRELLIS_E_ALIGN;
+  if (two && (!aligned(codes2, 16) || !aligned(scales2, 2))) return TRELLIS_E_ALIGN;
+  const uint16_t *xr[kMaxRows];
+  uint16_t *orow[kMaxRows];
+  for (int i = 0; i < m; ++i) {
+    xr[i] = x_bf16 + (size_t)i * g.k;
+    orow[i] = out_bf16 + (size_t)i * g.n;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  return launch_rows(xr, orow, m, codes, scales_bf16, codes2, scales2, g,
+                     reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 }  // namespace
@@ -1091,6 +1153,43 @@ trellis_status trellis_matvec(const uint16_t *x_bf16, int32_t m, const uint32_t 
   if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
   if (m < 1 || m > TRELLIS_MATVEC_MAX_M) return TRELLIS_E_M;
   return launch_linear(x_bf16, m, codes, scales_bf16, nullptr, nullptr, g, out_bf16, hip_stream);
+}
+
+trellis_status trellis_prefill_packed(const uint16_t *const *x_groups, const int32_t *rows, int32_t groups,
+                                      const uint32_t *codes, const uint16_t *scales_bf16, trellis_geom g,
+                                      uint16_t *const *out_groups, void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (!x_groups || !rows || !out_groups || !codes || !scales_bf16) return TRELLIS_E_NULL;
+  if (groups < 1 || groups > TRELLIS_MAX_GROUPS) return TRELLIS_E_M;
+  int64_t total = 0;
+  for (int32_t i = 0; i < groups; ++i) {
+    if (rows[i] < 0 || rows[i] > TRELLIS_MAX_GROUP_ROWS) return TRELLIS_E_M;
+    total += rows[i];
+    if (rows[i] == 0) continue;
+    if (!x_groups[i] || !out_groups[i]) return TRELLIS_E_NULL;
+    if (!aligned(x_groups[i], 16) || !aligned(out_groups[i], 16)) return TRELLIS_E_ALIGN;
+  }
+  if (total < 1) return TRELLIS_E_M;
+  if (!aligned(codes, 16) || !aligned(scales_bf16, 2)) return TRELLIS_E_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  // Packed rows in group order, in launches of at most TRELLIS_MAX_M rows.
+  const uint16_t *xr[kMaxRows];
+  uint16_t *orow[kMaxRows];
+  int n = 0;
+  for (int32_t i = 0; i < groups; ++i) {
+    for (int32_t r = 0; r < rows[i]; ++r) {
+      xr[n] = x_groups[i] + (size_t)r * g.k;
+      orow[n] = out_groups[i] + (size_t)r * g.n;
+      if (++n == TRELLIS_MAX_M) {
+        const trellis_status rc = launch_rows(xr, orow, n, codes, scales_bf16, nullptr, nullptr, g, stream);
+        if (rc != TRELLIS_OK) return rc;
+        n = 0;
+      }
+    }
+  }
+  if (n > 0) return launch_rows(xr, orow, n, codes, scales_bf16, nullptr, nullptr, g, stream);
+  return TRELLIS_OK;
 }
 
 trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m, const uint32_t *codes_gate,
