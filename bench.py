@@ -167,12 +167,30 @@ def main():
     lib = tp.load_library()
 
     # M = 1..4 is the matvec entry point (same kernel and decode); two
-    # matrices are the fused gate/up entry point.
+    # matrices are the fused gate/up entry point; packed workloads pass each
+    # input's rows as a separate allocation to trellis_prefill_packed.
     entry = lib.trellis_matvec if shape.m < tp.MIN_M else lib.trellis_prefill
+    packed = []
+    if shape.groups:
+        import ctypes
+
+        G = len(shape.groups)
+        for xs, _, out in sets:
+            xg, og, r0 = [], [], 0
+            for r in shape.groups:
+                xg.append(xs[r0:r0 + r].clone())
+                og.append(torch.empty((r, shape.n), dtype=torch.bfloat16, device=dev))
+                r0 += r
+            packed.append(((ctypes.c_void_p * G)(*[t.data_ptr() for t in xg]),
+                           (ctypes.c_void_p * G)(*[t.data_ptr() for t in og]), xg, og))
+        rows_arr = (ctypes.c_int32 * G)(*shape.groups)
 
     def step(i):
         xp, mp, op = ptrs[i % nsets]
-        if shape.matrices == 2:
+        if shape.groups:
+            xa, oa, _, _ = packed[i % nsets]
+            rc = lib.trellis_prefill_packed(xa, rows_arr, len(shape.groups), mp[0], mp[1], g, oa, handle)
+        elif shape.matrices == 2:
             rc = lib.trellis_gate_up(xp, shape.m, mp[0], mp[1], mp[2], mp[3], g, op, handle)
         else:
             rc = entry(xp, shape.m, mp[0], mp[1], g, op, handle)
@@ -231,7 +249,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": shape.name, "m": shape.m, "k": shape.k, "n": shape.n, "bits": shape.bits,
-                   "T": 256, "L": 12, "matrices": shape.matrices, "input_sets": nsets,
+                   "T": 256, "L": 12, "matrices": shape.matrices, "groups": list(shape.groups), "input_sets": nsets,
                    "mode": "warm" if args.warm else "cold"},
         "gweights_per_s": round(shape.weights / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {

@@ -41,6 +41,7 @@ class Shape:
     seed: int
     x_kind: str = "rmsnorm"   # "rmsnorm" or "silu_mul"
     matrices: int = 1         # 2: gate and up projections of the same x
+    groups: tuple = ()        # token packing: row counts of the packed inputs (sum = m)
 
     @property
     def words_per_row(self) -> int:
@@ -69,6 +70,8 @@ SHAPES = {
     "matvec_m4_k2": Shape("matvec_m4_k2", 4, 5120, 17408, 2, 7),
     # fused gate + up projections of one x (two code streams of this geometry)
     "gateup_m5_k4": Shape("gateup_m5_k4", 5, 5120, 17408, 4, 8, "rmsnorm", 2),
+    # token packing: three inputs of 5 rows each through one launch
+    "packed_3x5_k4": Shape("packed_3x5_k4", 15, 5120, 17408, 4, 9, "rmsnorm", 1, (5, 5, 5)),
 }
 
 
