@@ -35,21 +35,23 @@
  *   K % 256 == 0, 256 <= K <= TRELLIS_MAX_K;
  *   N % 4 == 0, 4 <= N <= TRELLIS_MAX_N;
  *   5 <= M <= 15 for trellis_prefill (the narrow-batch regime of the page's
- *   eligibility predicate), 1 <= M <= 4 for trellis_matvec;
+ *   eligibility predicate), 1 <= M <= 4 for trellis_matvec, 1 <= M <= 15
+ *   for trellis_gate_up, any number of packed rows for
+ *   trellis_prefill_packed (see there);
  *   x, codes, out and w 16-byte aligned; scales 2-byte aligned; no pointer
  *   NULL. The page's fixed K = 5120 is generalised to any multiple of 256.
  *
  * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns without waiting. trellis_decode keeps no
- * state. trellis_prefill, trellis_matvec and trellis_gate_up sum tiles that
- * are split across workgroups through a workspace (float32 partial tiles
- * and per-tile counters; for trellis_gate_up also the two bf16 projections)
- * owned by the library, one per (device, stream): it is allocated with
- * hipMalloc on the first call that needs it, grown (never shrunk or freed)
- * when a later call on that stream needs more, and kept until the process
- * exits; the kernel leaves its counters at zero for the next call. Calls on different
- * streams therefore never share a workspace; calls on one stream are
- * ordered by the stream. Host-side state is guarded by a mutex, so calls
+ * state. The other calls sum tiles that are split across workgroups
+ * through a workspace (float32 partial tiles and per-tile counters; for
+ * trellis_gate_up also the two bf16 projections) owned by the library, one
+ * per (device, stream): it is allocated with hipMalloc on the first call
+ * that needs it, grown (never shrunk or freed) when a later call on that
+ * stream needs more, and kept until the process exits; the kernel leaves
+ * its counters at zero for the next call. Calls on different streams
+ * therefore never share a workspace; calls on one stream are ordered by
+ * the stream. Host-side state is guarded by a mutex, so calls
  * may come from several threads. Errors are returned, never thrown; a
  * validation error leaves every output untouched.
  *
