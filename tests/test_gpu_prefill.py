@@ -199,3 +199,29 @@ def test_prefill_workspace_grows_between_calls():
                                                                         np.arange(0, n, 37)]))
         y, a = oracle.prefill_rows(x, codes, scales, k, bits, rows)
         assert_prefill_close(out[:, rows], y, a, f"growth m={m} k={k} n={n}")
+
+
+def test_prefill_maximum_k():
+    # K = TRELLIS_MAX_K (1024 blocks) at M = 15: x is staged in 64 K panels
+    # of 16 blocks; every tile is summed across panels through the workspace.
+    import torch
+
+    m, k, n, bits = 15, 1 << 18, 36, 2
+    print(f"prefill max K m={m} k={k} n={n}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=4300)
+    out = gpu_prefill(x, codes, scales, bits)
+    y, a = oracle.prefill(x, codes, scales, k, bits)
+    assert_prefill_close(out, y, a, "max K")
+
+
+def test_prefill_maximum_n():
+    # N = TRELLIS_MAX_N (2^18 tiles) with one block per row: a quarter of a
+    # million tiles spread over the workgroups; sampled rows checked.
+    m, k, n, bits = 7, 256, 1 << 22, 2
+    print(f"prefill max N m={m} k={k} n={n}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=4400)
+    out = gpu_prefill(x, codes, scales, bits)
+    rng = np.random.default_rng(14)
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(n - 40, n), rng.integers(0, n, 400)]))
+    y, a = oracle.prefill_rows(x, codes, scales, k, bits, rows)
+    assert_prefill_close(out[:, rows], y, a, "max N")
