@@ -16,13 +16,15 @@
 //     most one unit per SIMD (stream-K); waves rank themselves by the work
 //     they have left;
 //   * x is staged once per workgroup in LDS (a K panel of it when all of x
-//     does not fit) with an all-zero row that pads M up to 16;
+//     does not fit), read and written through per-row pointers so packed
+//     inputs need no copy;
 //   * each lane reads the code words of 64 consecutive weights of one row
 //     through a buffer descriptor and decodes them in registers, part of them
-//     through an LDS table (window -> value, or for k = 2 a 14-bit pair of
-//     windows -> two codes) and part with ALU arithmetic, so LDS and VALU
-//     work in parallel;
-//   * bf16 MFMA 16x16x32: A = x (rows padded to 16), B = W^T (16 rows);
+//     through an LDS table (window -> value, window -> float16 code, or for
+//     k = 2 a 14-bit pair of windows -> two codes) and part with ALU
+//     arithmetic, so LDS and VALU work in parallel;
+//   * bf16 MFMA 16x16x32: A = x (rows past M repeat row M-1 and feed output
+//     rows that are never stored), B = W^T (16 rows);
 //   * tiles shared by pieces of one workgroup are summed through LDS, tiles
 //     shared with other workgroups through a workspace, in a fixed order
 //     either way, the last contributor (per-tile counter) writing bf16.
@@ -906,7 +908,7 @@ __global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t *__restrict
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
-// use ALU arithmetic. PAIR: k = 2 with the pair table.
+// use ALU arithmetic. Mix<2, true>: k = 2 with the pair table.
 template <int BITS, bool PAIR = false> struct Mix;
 template <> struct Mix<2> { static constexpr int kMask = 0b11110000; };
 template <> struct Mix<2, true> { static constexpr int kMask = 0b11111111; };
