@@ -61,6 +61,7 @@ constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
 constexpr int kStageRegs = 10;             // x-staging vectors (16 B) per thread
 constexpr int kCombineBytes = kWaves * 2 * kWave * 16;  // LDS partial tiles of the end-of-kernel combine
+constexpr int kCombineCounters = kWaves * 4;             // LDS counters of the barrier-free combine
 static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(kCodeTable), "x staging must cover the largest panel");
 
 // ---------------------------------------------------------------------------
@@ -125,6 +126,8 @@ struct Plan {
   int32_t cr;        // units % groups: the first cr workgroups get cq + 1
   uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
   int32_t x_contiguous;  // 1: x row i is at row 0 + i * K (plain calls); 0: per-row pointers
+  int32_t slots_off;     // > 0: byte offset of dedicated partial-tile slots after x (LDS combine
+                         // without barriers); 0: slots reuse the x region after a barrier
 };
 
 // Split of a workgroup's contiguous units [u0, u0 + len) into s <= 16
@@ -697,6 +700,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       for (int r = 0; r < kMaxRows; ++r)
         if (lane == r) v = reinterpret_cast<uint64_t>(rp.out[r]);
       if (lane < kMaxRows) s_rows[lane] = v;
+      // counters of the barrier-free combine start at zero
+      if (pl.slots_off > 0 && lane < kWaves)
+        reinterpret_cast<uint32_t *>(xl + pl.slots_off + kCombineBytes)[lane] = 0u;
     }
     request(S0);
     if constexpr (TAB == kPairTable) {
@@ -739,11 +745,42 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   auto stage = [&](int t, f32x4 v) {
     stage_partial(partial_slot(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane), v);
   };
+  // Barrier-free combine (dedicated slots): the piece's partial of tile T
+  // goes to its slot (0: T is where the piece starts, 1: T is where it
+  // ends), and an LDS counter keyed by the position of the piece holding
+  // T's first unit counts the contributions. The piece that arrives last
+  // adds the partials in position order and stores bf16. Its slot write
+  // completes before its counter update, and the last arriver reads only
+  // after its own update returned, so it sees every partial.
+  auto contribute = [&](int T, f32x4 v, int which) {
+    f32x4 *slots = reinterpret_cast<f32x4 *>(xl + pl.slots_off);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(xl + pl.slots_off + kCombineBytes);
+    slots[(seg * 2 + which) * kWave + lane] = v;
+    const int p0 = piece_of(T * pl.kp, pl);
+    const int lead = p0 - group * kWaves;
+    const int contrib = piece_of(T * pl.kp + pl.kp - 1, pl) - p0 + 1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&cnt[lead], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    asm volatile("" ::: "memory");
+    if ((int)old + 1 != contrib) return;
+    const int t0u = T * pl.kp;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int sidx = lead; sidx < lead + contrib; ++sidx) {
+      const f32x4 w = slots[(sidx * 2 + (piece_start(q, sidx) >= t0u ? 0 : 1)) * kWave + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += w[e];
+    }
+    store_tile(s_rows, sum, pl.m, pl.out_rows, T * 16 + j, g);
+  };
   // A tile finished inside the loop is never the range's last tile.
   auto tile_done = [&](int t, f32x4 v) {
     if (cross(t)) stage(t, v);
-    else if (t == tf && u0 > t * pl.kp) part_f = v;
-    else store_tile(s_rows, v, pl.m, pl.out_rows, t * 16 + j, g);
+    else if (t == tf && u0 > t * pl.kp) {
+      if (pl.slots_off > 0) contribute(t, v, 0);
+      else part_f = v;
+    } else store_tile(s_rows, v, pl.m, pl.out_rows, t * 16 + j, g);
   };
   if (active) {
     int cur = tile;
@@ -805,6 +842,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     tl = cur;
     if (cross(cur)) stage(cur, acc);
     else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(s_rows, acc, pl.m, pl.out_rows, cur * 16 + j, g);
+    else if (pl.slots_off > 0) contribute(cur, acc, cur == tf ? 0 : 1);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
@@ -838,6 +876,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       }
     }
   }
+
+  if (pl.slots_off > 0) return;  // shared tiles were combined without barriers
 
   // ---- Combine the CU's own shared tiles through LDS. Segment s of the CU
   // holds a partial of its first tile when its range does not cover that
@@ -976,6 +1016,13 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   // Dynamic LDS: the x panel, later reused for the pieces' partial tiles
   // (two 16x16 fp32 tiles per wave).
   int need = m * pl.x_stride;
+  // Partial-tile slots of their own (after x) when they fit: the waves then
+  // combine shared tiles without barriers. Otherwise they reuse x's space.
+  pl.slots_off = 0;
+  if (table + kRowTableBytes + need + kCombineBytes + kCombineCounters <= kMaxLds) {
+    pl.slots_off = need;
+    need += kCombineBytes + kCombineCounters;
+  }
   if (need < kCombineBytes) need = kCombineBytes;
   const int fixed = table + kRowTableBytes;  // static LDS: decode table and row table
   pl.lds_bytes = need + fixed > kMinLds ? need : kMinLds - fixed;
