@@ -44,9 +44,8 @@
  * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
  * the default stream) and returns without waiting. trellis_decode keeps no
  * state. The other calls sum tiles that are split across workgroups
- * through a workspace (float32 partial tiles and per-tile counters; for
- * trellis_gate_up also the two bf16 projections) owned by the library, one
- * per (device, stream): it is allocated with hipMalloc on the first call
+ * through a workspace (float32 partial tiles and per-tile counters) owned
+ * by the library, one per (device, stream): it is allocated with hipMalloc on the first call
  * that needs it, grown (never shrunk or freed) when a later call on that
  * stream needs more, and kept until the process exits; the kernel leaves
  * its counters at zero for the next call. Calls on different streams
@@ -165,9 +164,10 @@ trellis_status trellis_prefill_packed(const uint16_t *const *x_groups, const int
  * (page "mlx-bun 0.0.4" (npm, page 62), section src/model/minicpm5.ts, MLP
  * forward); sigmoid is evaluated in float32. Wg and Wu share the geometry g
  * (same N, K and bits) and the formats above; 1 <= m <= 15. One launch
- * decodes both code streams against one staging of x into two bf16
- * projections held in the library's per-stream scratch (M x 32*ceil(N/16)
- * values), and a second, elementwise launch writes h. */
+ * decodes both code streams against one staging of x, each block of a gate
+ * tile next to the same block of the up tile, so the wave that completes a
+ * tile holds both float32 sums and writes h; the projections never reach
+ * memory. */
 trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m,
                                const uint32_t *codes_gate, const uint16_t *scales_gate,
                                const uint32_t *codes_up, const uint16_t *scales_up,

@@ -69,13 +69,26 @@ def test_gate_up_full_shape():
 
 def test_gate_up_k_panels():
     # x too large for one LDS panel: every tile of both matrices is summed
-    # across workgroups before the elementwise tail.
+    # across workgroups, and the last contributor writes the elementwise tail.
     print("gate_up k panels", flush=True)
     m, k, n, bits = 15, 17408, 260, 4
     x, cg, sg = generate(m, k, n, bits, seed=9001, x_kind="silu_mul")
     _, cu, su = generate(m, k, n, bits, seed=9002)
     h = gpu_gate_up(x, cg, sg, cu, su, bits)
     check(h, x, cg, sg, cu, su, k, bits, np.arange(n), "k panels")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_gate_up_partials_through_workspace(bits):
+    # M = 15 at K = 5120: x fills the LDS, so the gate and up partials have no
+    # LDS slots of their own and every shared tile is summed through the
+    # workspace; short pieces put about twenty contributors on each tile.
+    m, k, n = 15, 5120, 2000
+    print(f"gate_up workspace partials bits={bits}", flush=True)
+    x, cg, sg = generate(m, k, n, bits, seed=9201 + bits)
+    _, cu, su = generate(m, k, n, bits, seed=9301 + bits)
+    h = gpu_gate_up(x, cg, sg, cu, su, bits)
+    check(h, x, cg, sg, cu, su, k, bits, np.arange(n), f"workspace partials bits={bits}")
 
 
 def test_gate_up_deterministic():

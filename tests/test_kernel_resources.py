@@ -43,4 +43,6 @@ def test_prefill_kernels_use_no_scratch_and_fit_four_waves_per_simd():
         assert scratch == 0, f"{name} uses {scratch} bytes of scratch"
         assert vgprs <= 128, f"{name} uses {vgprs} VGPRs"
         seen += 1
-    assert seen == 7, f"expected 7 prefill kernels, found {seen}"
+    # k = 2, 3, 4 x (value, code table) + the pair table, each for one matrix
+    # and for the fused gate and up projections
+    assert seen == 14, f"expected 14 prefill kernels, found {seen}"

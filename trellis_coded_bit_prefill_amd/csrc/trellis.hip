@@ -61,6 +61,7 @@ constexpr int kMaxLds = 160 * 1024;        // gfx950 LDS per workgroup
 constexpr int kMinLds = 82 * 1024;         // > half the LDS: one workgroup per CU
 constexpr int kStageRegs = 10;             // x-staging vectors (16 B) per thread
 constexpr int kCombineBytes = kWaves * 2 * kWave * 16;  // LDS partial tiles of the end-of-kernel combine
+                                                        // (per matrix: twice that for gate and up)
 constexpr int kCombineCounters = kWaves * 4;             // LDS counters of the barrier-free combine
 static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(kCodeTable), "x staging must cover the largest panel");
 
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint32_t *__restrict_
 // ---------------------------------------------------------------------------
 
 // Rows of x and of the output, one pointer each: row i of x is
-// x[i][0 .. K), row i of the output out[i][0 .. out_rows). Rows of one
+// x[i][0 .. K), row i of the output out[i][0 .. N). Rows of one
 // array are consecutive for a plain call; packed calls gather rows of
 // several arrays. Entries past m are unused.
 struct RowPtrs {
@@ -112,16 +113,15 @@ struct RowPtrs {
 // Work partition, computed on the host and re-derived by every wave.
 struct Plan {
   int32_t m, n, k;
-  int32_t tiles;     // ceil(N / 16), or twice that for two matrices
-  int32_t half;      // two matrices: tiles of the first (the second's start); 0 for one
-  int32_t out_rows;  // columns of an output row: N, or 32 * half for two matrices
+  int32_t tiles;     // ceil(N / 16)
   int32_t panels;    // K panels (x panel staged per workgroup)
   int32_t kp;        // 256-weight blocks per panel
   int32_t groups;    // workgroups per panel
   int32_t maxc;      // contributor slots per (tile, panel) in the workspace
   int32_t x_stride;  // bytes per staged x row
   int32_t lds_bytes;
-  int32_t units;     // tiles * kp (per panel), < 2^28
+  int32_t units;     // tiles * kp (per panel), < 2^28; with two matrices a unit is the
+                     // same block of both
   int32_t cq;        // units / groups: every workgroup gets cq or cq + 1 units
   int32_t cr;        // units % groups: the first cr workgroups get cq + 1
   uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
@@ -505,20 +505,43 @@ __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned ch
   (unit_group<BITS, MASK, TAB, EXACT, U>(L, table, xa, s, q, k, mask, acc), ...);
 }
 
+// The MLP's elementwise tail on one output element, as the page's model
+// code orders it (page "mlx-bun 0.0.4" (npm, page 62), section
+// src/model/minicpm5.ts, MLP forward): every operation there yields a bf16
+// array, so the two projections, sigmoid(gate), gate * sigmoid(gate) and
+// that times up are each rounded to bf16. `gate` and `up` are the float32
+// sums of the two projections.
+__device__ __forceinline__ uint16_t gate_up_bits(float gate_sum, float up_sum) {
+  const float gate = (float)(__bf16)gate_sum, up = (float)(__bf16)up_sum;
+  const float sig = (float)(__bf16)(1.0f / (1.0f + expf(-gate)));
+  const float silu = (float)(__bf16)(gate * sig);
+  return __builtin_bit_cast(uint16_t, (__bf16)(silu * up));
+}
+
 // Lane (j, g) holds rows 4g .. 4g+3 of output column `col`; the row
-// pointers come from the LDS copy of the row table.
-__device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, int m, int ncols, int col, int g) {
+// pointers come from the LDS copy of the row table. One matrix: v is the
+// tile's sum. Two (gate and up): v and v2 are the two projections' sums and
+// the output is the elementwise tail.
+template <bool TWO>
+__device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, f32x4 v2, int m, int ncols, int col,
+                                           int g) {
   if (col >= ncols) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (4 * g + e < m)
-      reinterpret_cast<uint16_t *>(rows[4 * g + e])[col] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+    if (4 * g + e < m) {
+      uint16_t bits;
+      if constexpr (TWO) bits = gate_up_bits(v[e], v2[e]);
+      else bits = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+      reinterpret_cast<uint16_t *>(rows[4 * g + e])[col] = bits;
+    }
 }
 
 // Partials of tiles shared with other workgroups go through the workspace:
-// slot [tile][panel][contributor] holds one 16x16 fp32 partial, lane-major.
+// slot [tile][panel][contributor] holds NH 16x16 fp32 partials (one per
+// matrix), lane-major, 1 KB each.
+template <int NH>
 __device__ __forceinline__ float *partial_slot(const Plan &pl, float *ws, int tile, int panel, int idx, int lane) {
-  return ws + (((int64_t)tile * pl.panels + panel) * pl.maxc + idx) * 256 + 4 * lane;
+  return ws + ((((int64_t)tile * pl.panels + panel) * pl.maxc + idx) * NH) * 256 + 4 * lane;
 }
 
 // Stores a lane's four partial sums without making the wave wait for them:
@@ -539,26 +562,31 @@ __device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
       : "memory");
 }
 
-// Sum of a tile's staged partials, panel-major then contributor order. The
-// loads (16 bytes per lane, sc1: from the coherent level) are issued in
-// batches of sixteen slots before any of them is used, so a batch costs one
-// round trip rather than sixteen.
-__device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int tile, int contrib, int lane) {
+// Sums of a tile's staged partials (one per matrix), panel-major then
+// contributor order. The loads (16 bytes per lane, sc1: from the coherent
+// level) are issued in batches of sixteen 1 KB partials before any of them
+// is used, so a batch costs one round trip rather than sixteen. The batch
+// size is a multiple of NH, so load i of a batch belongs to matrix i % NH.
+template <int NH>
+__device__ __forceinline__ void sum_partials(const Plan &pl, float *ws, int tile, int contrib, int lane,
+                                             f32x4 (&sum)[NH]) {
   constexpr int kBatch = 16;
+  static_assert(kBatch % NH == 0, "a batch holds whole slots");
   constexpr int kSc1 = 16;  // cache-policy bits of the loads
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      partial_slot(pl, ws, tile, 0, 0, 0), (short)0, pl.panels * pl.maxc * 1024, kRawBufferWord3);
-  const int total = contrib * pl.panels;
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      partial_slot<NH>(pl, ws, tile, 0, 0, 0), (short)0, pl.panels * pl.maxc * NH * 1024, kRawBufferWord3);
+  const int total = contrib * pl.panels * NH;  // 1 KB partials
+#pragma unroll
+  for (int h = 0; h < NH; ++h) sum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   int pp = 0, cc = 0;  // slot of the next load
   for (int b0 = 0; b0 < total; b0 += kBatch) {
     f32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       // past the end: reload the last slot (valid memory, never added)
-      const uint32_t off = (uint32_t)(pp * pl.maxc + cc) * 1024 + (uint32_t)lane * 16;
+      const uint32_t off = ((uint32_t)(pp * pl.maxc + cc) * NH + (uint32_t)(i % NH)) * 1024 + (uint32_t)lane * 16;
       v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
-      if (b0 + i + 1 < total && ++cc == contrib) {
+      if (i % NH == NH - 1 && b0 + i + 1 < total && ++cc == contrib) {
         cc = 0;
         ++pp;
       }
@@ -567,12 +595,15 @@ __device__ __forceinline__ f32x4 sum_partials(const Plan &pl, float *ws, int til
     for (int i = 0; i < kBatch; ++i)
       if (b0 + i < total)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sum[e] += v[i][e];
+        for (int e = 0; e < 4; ++e) sum[i % NH][e] += v[i][e];
   }
-  return sum;
 }
 
-template <int BITS, int MASK, int TAB>
+// TWO: the fused gate and up projections. A unit is then one block of a tile
+// of both matrices, decoded in two steps (gate, then up) against the same x
+// into two accumulators, so whichever wave completes a tile holds both sums
+// and writes the elementwise tail directly.
+template <int BITS, int MASK, int TAB, bool TWO>
 __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
                                                              const uint32_t *__restrict__ codes2,
@@ -582,6 +613,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
   // After the main loop the x region is reused for the waves' partial tiles.
+  constexpr int NH = TWO ? 2 : 1;  // accumulators (matrices) per unit
+  constexpr int kSlotBytes = kCombineBytes * NH;
   __shared__ __attribute__((aligned(16))) uint32_t s_table[table_bytes(TAB) / 4];
   __shared__ uint64_t s_rows[kMaxRows];  // output row pointers
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -606,8 +639,12 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   const int u1 = active ? piece_start(q, seg + 1) : 0;
   const int piece = group * kWaves + seg;
   // A tile is "cross" when some of its units (of any panel) belong to another
-  // workgroup; its partials are combined through the workspace.
-  auto cross = [&](int t) { return pl.panels > 1 || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1; };
+  // workgroup; its partials are combined through the workspace. With two
+  // matrices and no LDS of their own for the partials (large x), every tile
+  // goes through the workspace.
+  auto cross = [&](int t) {
+    return pl.panels > 1 || (TWO && pl.slots_off == 0) || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1;
+  };
 
   // Per-lane byte offsets of the code words inside a unit's buffer (see
   // load_words) and of the row scale inside its tile's scale buffer.
@@ -615,25 +652,20 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   const uint32_t lane_off = (uint32_t)j * row_bytes + (uint32_t)g * (8 * BITS);
   const uint32_t lane_off_next = (uint32_t)j * row_bytes + (uint32_t)((2 * BITS * (g + 1)) % wpb) * 4;
   const uint32_t lane_off_scale = (uint32_t)j * 2;
-  // Buffers of unit (t, bb) and of tile t's scales: rows past N are outside
-  // them, so their words and scales read as zero (zero weights, never stored).
-  // With two matrices (gate and up), tiles [half, tiles) are the second
-  // matrix's tiles 0, 1, ...
-  auto unit_buffer = [&](int t, int bb) {
-    const bool second = pl.half > 0 && t >= pl.half;
-    const int tt = second ? t - pl.half : t;
-    const int rows = pl.n - tt * 16 < 16 ? pl.n - tt * 16 : 16;
+  // Buffers of unit (t, bb) and of tile t's scales, of the first matrix or
+  // (second) of the up matrix: rows past N are outside them, so their words
+  // and scales read as zero (zero weights, never stored).
+  auto unit_buffer = [&](int t, int bb, bool second) {
+    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
     const uint32_t blk_off = (uint32_t)(panel * pl.kp + bb) * (wpb * 4);
     const unsigned char *base = reinterpret_cast<const unsigned char *>(second ? codes2 : codes) +
-                                (int64_t)tt * 16 * row_bytes + blk_off;
+                                (int64_t)t * 16 * row_bytes + blk_off;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(base), (short)0,
                                              (int)((uint32_t)rows * row_bytes - blk_off), kRawBufferWord3);
   };
-  auto scale_buffer = [&](int t) {
-    const bool second = pl.half > 0 && t >= pl.half;
-    const int tt = second ? t - pl.half : t;
-    const int rows = pl.n - tt * 16 < 16 ? pl.n - tt * 16 : 16;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((second ? scales2 : scales) + (int64_t)tt * 16),
+  auto scale_buffer = [&](int t, bool second) {
+    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((second ? scales2 : scales) + (int64_t)t * 16),
                                              (short)0, rows * 2, kRawBufferWord3);
   };
   // Raw scale bits are converted only when the tile starts, so the load is
@@ -643,7 +675,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // Code words (and the row scale) of each unit live in one of two register
   // slots: the unit being decoded and the next one in flight. The loop below
   // is unrolled by two so the slots alternate without copying registers that
-  // still have loads pending.
+  // still have loads pending. With two matrices slot 0 always holds a gate
+  // block and slot 1 the same block of up.
   struct Slot {
     LaneWords<BITS> w;
     uint32_t scb;  // raw bf16 scale bits
@@ -661,10 +694,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // Every loop iteration requests the same number of units (straight-line
   // code keeps the compiler's memory-counter waits exact); the step of the
   // range's last unit requests nothing, so requests never leave the range.
-  auto request = [&](Slot &S) {
-    load_words<BITS>(unit_buffer(pt, pb), lane_off, lane_off_next, S.w);
-    S.scb = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(pt), lane_off_scale, 0, 0);
-    if (++pu < u1) advance(pt, pb);
+  auto request = [&](Slot &S, auto second) {
+    constexpr bool kUp = decltype(second)::value;
+    load_words<BITS>(unit_buffer(pt, pb, kUp), lane_off, lane_off_next, S.w);
+    S.scb = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(pt, kUp), lane_off_scale, 0, 0);
+    if constexpr (!TWO || kUp) {
+      if (++pu < u1) advance(pt, pb);
+    }
   };
   // Prologue. x[:, panel] (M rows) is requested first, then the first unit's code words (memory-counter waits are in
   // issue order, so x can be stored to LDS without waiting for the codes);
@@ -702,9 +738,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       if (lane < kMaxRows) s_rows[lane] = v;
       // counters of the barrier-free combine start at zero
       if (pl.slots_off > 0 && lane < kWaves)
-        reinterpret_cast<uint32_t *>(xl + pl.slots_off + kCombineBytes)[lane] = 0u;
+        reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes)[lane] = 0u;
     }
-    request(S0);
+    request(S0, std::false_type{});
     if constexpr (TAB == kPairTable) {
       for (int e = tid; e < 16384; e += kWgThreads) s_table[e] = pair_entry((uint32_t)e);
     } else if constexpr (TAB == kCodeTable) {
@@ -741,9 +777,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // K panel only its first or last tile can be).
   const bool holds_cross =
       active && (cross(tf) || cross((int)((uint32_t)(u1 > 0 ? u1 - 1 : 0) / (uint32_t)pl.kp)));
+  // Partials kept for the barrier combine (one matrix only: with two, shared
+  // tiles use dedicated LDS slots or the workspace).
   f32x4 part_f = {0.f, 0.f, 0.f, 0.f}, part_l = {0.f, 0.f, 0.f, 0.f};
-  auto stage = [&](int t, f32x4 v) {
-    stage_partial(partial_slot(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane), v);
+  auto stage = [&](int t, f32x4 v, f32x4 v2) {
+    float *slot = partial_slot<NH>(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane);
+    stage_partial(slot, v);
+    if constexpr (TWO) stage_partial(slot + 256, v2);
   };
   // Barrier-free combine (dedicated slots): the piece's partial of tile T
   // goes to its slot (0: T is where the piece starts, 1: T is where it
@@ -752,10 +792,11 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // adds the partials in position order and stores bf16. Its slot write
   // completes before its counter update, and the last arriver reads only
   // after its own update returned, so it sees every partial.
-  auto contribute = [&](int T, f32x4 v, int which) {
-    f32x4 *slots = reinterpret_cast<f32x4 *>(xl + pl.slots_off);
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(xl + pl.slots_off + kCombineBytes);
-    slots[(seg * 2 + which) * kWave + lane] = v;
+  auto contribute = [&](int T, f32x4 v, f32x4 v2, int which) {
+    f32x4 *slots = reinterpret_cast<f32x4 *>(xl + pl.slots_off);  // [piece][first, last][matrix][lane]
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes);
+    slots[((seg * 2 + which) * NH) * kWave + lane] = v;
+    if constexpr (TWO) slots[((seg * 2 + which) * NH + 1) * kWave + lane] = v2;
     const int p0 = piece_of(T * pl.kp, pl);
     const int lead = p0 - group * kWaves;
     const int contrib = piece_of(T * pl.kp + pl.kp - 1, pl) - p0 + 1;
@@ -766,21 +807,27 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     asm volatile("" ::: "memory");
     if ((int)old + 1 != contrib) return;
     const int t0u = T * pl.kp;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int sidx = lead; sidx < lead + contrib; ++sidx) {
-      const f32x4 w = slots[(sidx * 2 + (piece_start(q, sidx) >= t0u ? 0 : 1)) * kWave + lane];
+    f32x4 sum[NH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum[e] += w[e];
+    for (int h = 0; h < NH; ++h) sum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sidx = lead; sidx < lead + contrib; ++sidx) {
+      const int base = (sidx * 2 + (piece_start(q, sidx) >= t0u ? 0 : 1)) * NH;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const f32x4 w = slots[(base + h) * kWave + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[h][e] += w[e];
+      }
     }
-    store_tile(s_rows, sum, pl.m, pl.out_rows, T * 16 + j, g);
+    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
   };
   // A tile finished inside the loop is never the range's last tile.
-  auto tile_done = [&](int t, f32x4 v) {
-    if (cross(t)) stage(t, v);
+  auto tile_done = [&](int t, f32x4 v, f32x4 v2) {
+    if (cross(t)) stage(t, v, v2);
     else if (t == tf && u0 > t * pl.kp) {
-      if (pl.slots_off > 0) contribute(t, v, 0);
+      if (TWO || pl.slots_off > 0) contribute(t, v, v2, 0);
       else part_f = v;
-    } else store_tile(s_rows, v, pl.m, pl.out_rows, t * 16 + j, g);
+    } else store_tile<TWO>(s_rows, v, v2, pl.m, pl.n, t * 16 + j, g);
   };
   if (active) {
     int cur = tile;
@@ -788,33 +835,51 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     float s = scale_of(S0.scb), q, kq;
     alu_row_constants(s, q, kq);
     bool out_of_range = !__all(alu_scale_ok(s));
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};  // second matrix (up)
     // table byte-address mask (SDWA operand)
     const uint32_t mask_addr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
     int u = u0;
     // Decode unit u from slot C while unit u + 1 is requested into slot N;
     // the range's last unit requests nothing (`last`), so no load is left in
-    // flight after the loop.
-    auto step = [&](Slot &C, Slot &N, auto last) {
-      if (tile != cur) {
-        tile_done(cur, acc);
-        cur = tile;
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        s = scale_of(C.scb);
-        alu_row_constants(s, q, kq);
-        out_of_range = !__all(alu_scale_ok(s));
+    // flight after the loop. With two matrices a unit takes two steps: the
+    // gate block (slot 0, which requests the up block of the same unit) and
+    // the up block (slot 1, which requests the next unit's gate block).
+    auto step = [&](Slot &C, Slot &N, auto last, auto second) {
+      constexpr bool kUp = decltype(second)::value;
+      f32x4 &A = kUp ? acc2 : acc;
+      if constexpr (!kUp) {
+        if (tile != cur) {
+          tile_done(cur, acc, acc2);
+          cur = tile;
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+          s = scale_of(C.scb);
+          alu_row_constants(s, q, kq);
+          out_of_range = !__all(alu_scale_ok(s));
+        }
       }
-      if constexpr (!decltype(last)::value) request(N);
+      // The up block's row constants come from its scale at every step
+      // (about 8 VALU ops; keeping a second set live spills registers).
+      float ss = s, qq = q, kk = kq;
+      bool oor = out_of_range;
+      if constexpr (kUp) {
+        ss = scale_of(C.scb);
+        alu_row_constants(ss, qq, kk);
+        oor = !__all(alu_scale_ok(ss));
+      }
+      if constexpr (!decltype(last)::value) request(N, std::bool_constant<TWO && !kUp>{});
       const unsigned char *xb = xa + b * 512;
       // Rows whose scale is outside the exact range of code * q: the value
       // table (with the code or pair table, the pages' chain on the ALU) for
       // every group.
-      if (out_of_range)
-        unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(C.w, table, xb, s, q, kq, mask_addr, acc,
+      if (oor)
+        unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(C.w, table, xb, ss, qq, kk, mask_addr, A,
                                                           std::make_integer_sequence<int, 8>{});
       else if constexpr (BITS == 4 && MASK == 0x33 && TAB != kPairTable)
-        unit4_phased<TAB>(C.w, table, xb, s, q, kq, mask_addr, acc);
+        unit4_phased<TAB>(C.w, table, xb, ss, qq, kk, mask_addr, A);
       else
-        unit<BITS, MASK, TAB, false>(C.w, table, xb, s, q, kq, mask_addr, acc, std::make_integer_sequence<int, 8>{});
+        unit<BITS, MASK, TAB, false>(C.w, table, xb, ss, qq, kk, mask_addr, A, std::make_integer_sequence<int, 8>{});
+      if constexpr (TWO && !kUp) return;  // the unit's up block follows
       advance(tile, b);
       ++u;
       // A SIMD issues from its highest-priority ready wave, oldest first
@@ -827,22 +892,26 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       else if (rem == 2) __builtin_amdgcn_s_setprio(2);
       else __builtin_amdgcn_s_setprio(1);
     };
+    using UpInSlot1 = std::bool_constant<TWO>;
     for (;;) {
+      if constexpr (!TWO) {
+        if (u + 1 == u1) {
+          step(S0, S1, std::true_type{}, std::false_type{});
+          break;
+        }
+      }
+      step(S0, S1, std::false_type{}, std::false_type{});
       if (u + 1 == u1) {
-        step(S0, S1, std::true_type{});
+        step(S1, S0, std::true_type{}, UpInSlot1{});
         break;
       }
-      step(S0, S1, std::false_type{});
-      if (u + 1 == u1) {
-        step(S1, S0, std::true_type{});
-        break;
-      }
-      step(S1, S0, std::false_type{});
+      step(S1, S0, std::false_type{}, UpInSlot1{});
     }
     tl = cur;
-    if (cross(cur)) stage(cur, acc);
-    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp) store_tile(s_rows, acc, pl.m, pl.out_rows, cur * 16 + j, g);
-    else if (pl.slots_off > 0) contribute(cur, acc, cur == tf ? 0 : 1);
+    if (cross(cur)) stage(cur, acc, acc2);
+    else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp)
+      store_tile<TWO>(s_rows, acc, acc2, pl.m, pl.n, cur * 16 + j, g);
+    else if (TWO || pl.slots_off > 0) contribute(cur, acc, acc2, cur == tf ? 0 : 1);
     else if (cur == tf) part_f = acc;
     else part_l = acc;
   }
@@ -871,13 +940,15 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         last &= last - 1;
         const int T = t0 + i;
         const int c = __shfl(contrib, i);
-        store_tile(s_rows, sum_partials(pl, ws, T, c, lane), pl.m, pl.out_rows, T * 16 + j, g);
+        f32x4 sum[NH];
+        sum_partials<NH>(pl, ws, T, c, lane, sum);
+        store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
         if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
 
-  if (pl.slots_off > 0) return;  // shared tiles were combined without barriers
+  if (TWO || pl.slots_off > 0) return;  // shared tiles were combined without barriers
 
   // ---- Combine the CU's own shared tiles through LDS. Segment s of the CU
   // holds a partial of its first tile when its range does not cover that
@@ -918,33 +989,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
       if (e >= t1u) break;  // T ends in this segment
     }
-    store_tile(s_rows, sum, pl.m, pl.out_rows, T * 16 + j, g);
+    store_tile<false>(s_rows, sum, sum, pl.m, pl.n, T * 16 + j, g);
   }
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
-}
-
-// ---------------------------------------------------------------------------
-// gate_up_kernel: the MLP's elementwise tail on the two projections, as the
-// page's model code orders it (page "mlx-bun 0.0.4" (npm, page 62), section
-// src/model/minicpm5.ts, MLP forward): every operation yields a bf16 array,
-// so sigmoid(gate), gate * sigmoid(gate) and that times up are each rounded
-// to bf16. gu holds row i's gate values at [i * 2h, i * 2h + n) and its up
-// values at [i * 2h + h, ...), h = half_rows.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gate_up_kernel(const uint16_t *__restrict__ gu, int m, int n, int half_rows,
-                                                      uint16_t *__restrict__ h) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)m * n) return;
-  const int i = (int)(idx / n), c = (int)(idx - (int64_t)i * n);
-  const uint16_t *row = gu + (int64_t)i * 2 * half_rows;
-  const float gate = bf16_bits_to_f32(row[c]), up = bf16_bits_to_f32(row[half_rows + c]);
-  const float sig = (float)(__bf16)(1.0f / (1.0f + expf(-gate)));
-  const float silu = (float)(__bf16)(gate * sig);
-  h[idx] = __builtin_bit_cast(uint16_t, (__bf16)(silu * up));
 }
 
 // Which MFMA groups (bit u of the mask) decode through the LDS table; the rest
@@ -979,10 +1030,7 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   pl.m = m;
   pl.n = n;
   pl.k = k;
-  const int tiles = (n + 15) / 16;
-  pl.tiles = two ? 2 * tiles : tiles;
-  pl.half = two ? tiles : 0;
-  pl.out_rows = two ? 32 * tiles : n;
+  pl.tiles = (n + 15) / 16;
   const int kb = k / 256;
   int panels = kb;
   for (int p = 1; p <= kb; ++p) {
@@ -1017,11 +1065,13 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   // (two 16x16 fp32 tiles per wave).
   int need = m * pl.x_stride;
   // Partial-tile slots of their own (after x) when they fit: the waves then
-  // combine shared tiles without barriers. Otherwise they reuse x's space.
+  // combine shared tiles without barriers. Otherwise they reuse x's space
+  // (one matrix), or every shared tile goes through the workspace (two).
+  const int slot_bytes = kCombineBytes * (two ? 2 : 1);
   pl.slots_off = 0;
-  if (table + kRowTableBytes + need + kCombineBytes + kCombineCounters <= kMaxLds) {
+  if (table + kRowTableBytes + need + slot_bytes + kCombineCounters <= kMaxLds) {
     pl.slots_off = need;
-    need += kCombineBytes + kCombineCounters;
+    need += slot_bytes + kCombineCounters;
   }
   if (need < kCombineBytes) need = kCombineBytes;
   const int fixed = table + kRowTableBytes;  // static LDS: decode table and row table
@@ -1030,10 +1080,13 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
 }
 
 // Prefill kernels: k = 2, 3, 4 with the value or the code table, and k = 2
-// with the pair table. Variant = 2 * (k - 2) + table kind, pair = 6.
-enum Variant { kVariantPair = 6, kVariants = 7 };
-constexpr int variant_of(int bits, int tab) { return tab == kPairTable ? kVariantPair : 2 * (bits - 2) + tab; }
-constexpr int variant_table(int v) { return v == kVariantPair ? kPairTable : v % 2; }
+// with the pair table, each for one matrix or for gate and up. Variant =
+// 2 * (k - 2) + table kind, pair = 6; plus kTables for two matrices.
+enum Variant { kVariantPair = 6, kTables = 7, kVariants = 2 * kTables };
+constexpr int variant_of(int bits, int tab, bool two) {
+  return (tab == kPairTable ? kVariantPair : 2 * (bits - 2) + tab) + (two ? kTables : 0);
+}
+constexpr int variant_table(int v) { return v % kTables == kVariantPair ? kPairTable : v % kTables % 2; }
 
 struct DeviceState {
   int cus = 0;
@@ -1045,8 +1098,6 @@ struct Workspace {
   size_t ws_floats = 0;
   uint32_t *counters = nullptr;
   size_t ncounters = 0;
-  uint16_t *gu = nullptr;  // gate and up projections (bf16) of trellis_gate_up
-  size_t gu_elems = 0;
 };
 
 std::mutex g_mu;
@@ -1055,17 +1106,19 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 typedef void (*PrefillFn)(const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *, float *, uint32_t *,
                           Plan, RowPtrs);
-PrefillFn prefill_fn(int v) {
+template <bool TWO>
+PrefillFn prefill_fn_of(int v) {
   switch (v) {
-    case 0: return &prefill_kernel<2, Mix<2>::kMask, kValueTable>;
-    case 1: return &prefill_kernel<2, Mix<2>::kMask, kCodeTable>;
-    case 2: return &prefill_kernel<3, Mix<3>::kMask, kValueTable>;
-    case 3: return &prefill_kernel<3, Mix<3>::kMask, kCodeTable>;
-    case 4: return &prefill_kernel<4, Mix<4>::kMask, kValueTable>;
-    case 5: return &prefill_kernel<4, Mix<4>::kMask, kCodeTable>;
-    default: return &prefill_kernel<2, Mix<2, true>::kMask, kPairTable>;
+    case 0: return &prefill_kernel<2, Mix<2>::kMask, kValueTable, TWO>;
+    case 1: return &prefill_kernel<2, Mix<2>::kMask, kCodeTable, TWO>;
+    case 2: return &prefill_kernel<3, Mix<3>::kMask, kValueTable, TWO>;
+    case 3: return &prefill_kernel<3, Mix<3>::kMask, kCodeTable, TWO>;
+    case 4: return &prefill_kernel<4, Mix<4>::kMask, kValueTable, TWO>;
+    case 5: return &prefill_kernel<4, Mix<4>::kMask, kCodeTable, TWO>;
+    default: return &prefill_kernel<2, Mix<2, true>::kMask, kPairTable, TWO>;
   }
 }
+PrefillFn prefill_fn(int v) { return v >= kTables ? prefill_fn_of<true>(v - kTables) : prefill_fn_of<false>(v); }
 
 trellis_status device_state(DeviceState *&st, int v) {
   int dev = 0;
@@ -1110,15 +1163,6 @@ trellis_status workspace(hipStream_t stream, size_t ws_floats, size_t ncounters,
     w.ncounters = ncounters;
   }
   out = &w;
-  return TRELLIS_OK;
-}
-
-trellis_status gate_up_scratch(Workspace &w, size_t elems) {
-  if (w.gu_elems >= elems) return TRELLIS_OK;
-  uint16_t *p = nullptr;
-  if (hipMalloc(&p, elems * sizeof(uint16_t)) != hipSuccess) return TRELLIS_E_HIP;
-  w.gu = p;
-  w.gu_elems = elems;
   return TRELLIS_OK;
 }
 
@@ -1181,9 +1225,8 @@ int table_override(int bits) {
 // One launch of the layer on m <= 15 rows (any m >= 1 with a valid
 // geometry; the entry points restrict m to their regimes): x row i at
 // x_rows[i], output row i at out_rows[i]. With a second matrix (codes2,
-// scales2) both projections go to the gate/up scratch in the same launch,
-// and gate_up_kernel then writes silu(gate) * up to the [m, N] array at
-// out_rows[0] (rows consecutive).
+// scales2, the up projection) the output is the elementwise tail of the
+// two projections, from the same launch.
 trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_rows, int32_t m,
                            const uint32_t *codes, const uint16_t *scales_bf16, const uint32_t *codes2,
                            const uint16_t *scales2, trellis_geom g, hipStream_t stream) {
@@ -1191,7 +1234,7 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   int cus = 0;
   {
     DeviceState *st0 = nullptr;
-    const trellis_status rc0 = device_state(st0, variant_of(g.bits, kValueTable));
+    const trellis_status rc0 = device_state(st0, variant_of(g.bits, kValueTable, two));
     if (rc0 != TRELLIS_OK) return rc0;
     cus = st0->cus;
   }
@@ -1217,12 +1260,12 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
       }
     }
   }
-  const int v = variant_of(g.bits, tab);
+  const int v = variant_of(g.bits, tab, two);
   DeviceState *st = nullptr;
   trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
   Workspace *w = nullptr;
-  rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256, (size_t)pl.tiles, w);
+  rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256 * (two ? 2 : 1), (size_t)pl.tiles, w);
   if (rc != TRELLIS_OK) return rc;
   RowPtrs rp{};
   pl.x_contiguous = 1;
@@ -1230,13 +1273,7 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
     rp.x[i] = x_rows[i];
     if (x_rows[i] != x_rows[0] + (size_t)i * g.k) pl.x_contiguous = 0;
   }
-  if (two) {
-    rc = gate_up_scratch(*w, (size_t)m * pl.out_rows);
-    if (rc != TRELLIS_OK) return rc;
-    for (int i = 0; i < m; ++i) rp.out[i] = w->gu + (size_t)i * pl.out_rows;
-  } else {
-    for (int i = 0; i < m; ++i) rp.out[i] = out_rows[i];
-  }
+  for (int i = 0; i < m; ++i) rp.out[i] = out_rows[i];
   // Unused slots repeat row 0 (never dereferenced).
   for (int i = m; i < kMaxRows; ++i) {
     rp.x[i] = rp.x[0];
@@ -1246,11 +1283,6 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   clear_last_error();
   hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, codes, scales_bf16, codes2, scales2, w->ws,
                      w->counters, pl, rp);
-  if (two) {
-    const int64_t total = (int64_t)m * g.n;
-    hipLaunchKernelGGL(gate_up_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                       (const uint16_t *)w->gu, m, g.n, pl.half * 16, out_rows[0]);
-  }
   return launch_status();
 }
 
