@@ -79,16 +79,25 @@ def test_gate_up_k_panels():
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-def test_gate_up_partials_through_workspace(bits):
-    # M = 15 at K = 5120: x fills the LDS, so the gate and up partials have no
-    # LDS slots of their own and every shared tile is summed through the
-    # workspace; short pieces put about twenty contributors on each tile.
-    m, k, n = 15, 5120, 2000
-    print(f"gate_up workspace partials bits={bits}", flush=True)
-    x, cg, sg = generate(m, k, n, bits, seed=9201 + bits)
-    _, cu, su = generate(m, k, n, bits, seed=9301 + bits)
+@pytest.mark.parametrize("m,n", [(15, 2000), (15, 17408), (8, 17408)])
+def test_gate_up_barrier_combine(bits, m, n):
+    # M >= 8 at K = 5120: x leaves no LDS for partial slots of both
+    # matrices, so tiles shared inside a workgroup are summed after a barrier
+    # in x's LDS, and the pair of partials of a piece's first tile waits in
+    # global memory through the loop. N = 2000 gives one-unit pieces (about
+    # twenty contributors per tile); N = 17408 gives pieces of several units
+    # that start inside one tile and end in another.
+    k = 5120
+    print(f"gate_up barrier combine m={m} n={n} bits={bits}", flush=True)
+    x, cg, sg = generate(m, k, n, bits, seed=9201 + bits + m)
+    _, cu, su = generate(m, k, n, bits, seed=9301 + bits + m)
     h = gpu_gate_up(x, cg, sg, cu, su, bits)
-    check(h, x, cg, sg, cu, su, k, bits, np.arange(n), f"workspace partials bits={bits}")
+    if n <= 2000:
+        rows = np.arange(n)
+    else:
+        rng = np.random.default_rng(17)
+        rows = np.unique(np.concatenate([np.arange(48), np.arange(n - 48, n), rng.integers(0, n, 320)]))
+    check(h, x, cg, sg, cu, su, k, bits, rows, f"barrier combine m={m} n={n} bits={bits}")
 
 
 def test_gate_up_deterministic():

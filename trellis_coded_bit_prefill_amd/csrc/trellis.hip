@@ -526,13 +526,19 @@ template <bool TWO>
 __device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, f32x4 v2, int m, int ncols, int col,
                                            int g) {
   if (col >= ncols) return;
+  // The lane's row-table address is formed here, at the store: the empty
+  // asm keeps the compiler from hoisting it out of the main loop, where one
+  // more live register would spill.
+  int gr = 4 * g;
+  asm volatile("" : "+v"(gr));
+  const uint64_t *my_rows = rows + gr;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (4 * g + e < m) {
+    if (gr + e < m) {
       uint16_t bits;
       if constexpr (TWO) bits = gate_up_bits(v[e], v2[e]);
       else bits = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-      reinterpret_cast<uint16_t *>(rows[4 * g + e])[col] = bits;
+      reinterpret_cast<uint16_t *>(my_rows[e])[col] = bits;
     }
 }
 
@@ -559,6 +565,19 @@ __device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
       "s_nop 1"
       :
       : "v"(slot), "v"(v)
+      : "memory");
+}
+
+// The same for a pair of partials (two matrices) at a wave-uniform base:
+// lane offsets `off` and off + 1 KB. The address stays a scalar base plus a
+// 32-bit lane offset, so nothing 64-bit per lane has to be kept live.
+__device__ __forceinline__ void stage_pair(float *base, uint32_t off, f32x4 v, f32x4 v2) {
+  asm volatile(
+      "global_store_dwordx4 %0, %1, %3 sc1\n\t"
+      "global_store_dwordx4 %0, %2, %3 offset:1024 sc1\n\t"
+      "s_nop 1"
+      :
+      : "v"(off), "v"(v), "v"(v2), "s"(base)
       : "memory");
 }
 
@@ -609,7 +628,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
                                                              const uint32_t *__restrict__ codes2,
                                                              const uint16_t *__restrict__ scales2,
                                                              float *__restrict__ ws, uint32_t *__restrict__ counters,
-                                                             Plan pl, RowPtrs rp) {
+                                                             float *__restrict__ kept, Plan pl, RowPtrs rp) {
   // The table is static LDS (address known at compile time, so table reads
   // carry their base in the instruction offset); x follows it dynamically.
   // After the main loop the x region is reused for the waves' partial tiles.
@@ -639,12 +658,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   const int u1 = active ? piece_start(q, seg + 1) : 0;
   const int piece = group * kWaves + seg;
   // A tile is "cross" when some of its units (of any panel) belong to another
-  // workgroup; its partials are combined through the workspace. With two
-  // matrices and no LDS of their own for the partials (large x), every tile
-  // goes through the workspace.
-  auto cross = [&](int t) {
-    return pl.panels > 1 || (TWO && pl.slots_off == 0) || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1;
-  };
+  // workgroup; its partials are combined through the workspace.
+  auto cross = [&](int t) { return pl.panels > 1 || t * pl.kp < cu_u0 || (t + 1) * pl.kp > cu_u1; };
 
   // Per-lane byte offsets of the code words inside a unit's buffer (see
   // load_words) and of the row scale inside its tile's scale buffer.
@@ -777,9 +792,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // K panel only its first or last tile can be).
   const bool holds_cross =
       active && (cross(tf) || cross((int)((uint32_t)(u1 > 0 ? u1 - 1 : 0) / (uint32_t)pl.kp)));
-  // Partials kept for the barrier combine (one matrix only: with two, shared
-  // tiles use dedicated LDS slots or the workspace).
+  // Partials kept for the barrier combine: of the range's first tile (when
+  // it ends inside the loop) and of its last tile. With two matrices the
+  // first tile's pair waits in this wave's slot of `kept` (global memory)
+  // instead of registers, which the loop cannot spare.
   f32x4 part_f = {0.f, 0.f, 0.f, 0.f}, part_l = {0.f, 0.f, 0.f, 0.f};
+  f32x4 part_f2 = {0.f, 0.f, 0.f, 0.f}, part_l2 = {0.f, 0.f, 0.f, 0.f};
+  float *const kept_base = kept + ((int64_t)blockIdx.x * kWaves + wave) * 512;  // wave-uniform
   auto stage = [&](int t, f32x4 v, f32x4 v2) {
     float *slot = partial_slot<NH>(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane);
     stage_partial(slot, v);
@@ -825,7 +844,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   auto tile_done = [&](int t, f32x4 v, f32x4 v2) {
     if (cross(t)) stage(t, v, v2);
     else if (t == tf && u0 > t * pl.kp) {
-      if (TWO || pl.slots_off > 0) contribute(t, v, v2, 0);
+      if (pl.slots_off > 0) contribute(t, v, v2, 0);
+      else if constexpr (TWO) stage_pair(kept_base, (uint32_t)lane * 16, v, v2);
       else part_f = v;
     } else store_tile<TWO>(s_rows, v, v2, pl.m, pl.n, t * 16 + j, g);
   };
@@ -911,9 +931,14 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     if (cross(cur)) stage(cur, acc, acc2);
     else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp)
       store_tile<TWO>(s_rows, acc, acc2, pl.m, pl.n, cur * 16 + j, g);
-    else if (TWO || pl.slots_off > 0) contribute(cur, acc, acc2, cur == tf ? 0 : 1);
-    else if (cur == tf) part_f = acc;
-    else part_l = acc;
+    else if (pl.slots_off > 0) contribute(cur, acc, acc2, cur == tf ? 0 : 1);
+    else if (cur == tf) {
+      part_f = acc;
+      part_f2 = acc2;
+    } else {
+      part_l = acc;
+      part_l2 = acc2;
+    }
   }
 
   // ---- Publish the cross tiles of the range: once the staged partials are
@@ -948,17 +973,33 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
   }
 
-  if (TWO || pl.slots_off > 0) return;  // shared tiles were combined without barriers
+  if (pl.slots_off > 0) return;  // shared tiles were combined without barriers
+
+  // Two matrices: fetch the first tile's pair back from `kept` (its stores
+  // were issued in the loop and have completed by the wait).
+  if constexpr (TWO) {
+    if (active && tl != tf && u0 > tf * pl.kp && !cross(tf)) {
+      constexpr int kSc1 = 16;  // cache-policy bits of the loads
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(kept_base, (short)0, 2048, kRawBufferWord3);
+      part_f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)lane * 16, 0, kSc1));
+      part_f2 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 + (uint32_t)lane * 16, 0, kSc1));
+    }
+  }
 
   // ---- Combine the CU's own shared tiles through LDS. Segment s of the CU
   // holds a partial of its first tile when its range does not cover that
   // whole tile, and a partial of its last tile (when different) when its
   // range ends inside it; cross tiles went through the workspace.
   __syncthreads();  // all waves are done reading x; its LDS holds the partials now
-  f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [segment][first, last][lane]
+  f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [segment][first, last][matrix][lane]
   if (active) {
-    slots[(seg * 2 + 0) * kWave + lane] = part_f;
-    slots[(seg * 2 + 1) * kWave + lane] = part_l;
+    slots[(seg * 2 + 0) * NH * kWave + lane] = part_f;
+    slots[(seg * 2 + 1) * NH * kWave + lane] = part_l;
+    if constexpr (TWO) {
+      slots[((seg * 2 + 0) * NH + 1) * kWave + lane] = part_f2;
+      slots[((seg * 2 + 1) * NH + 1) * kWave + lane] = part_l2;
+    }
   }
   __syncthreads();
   if (!active) return;
@@ -977,19 +1018,24 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
     if (cross(T)) continue;
     const int t0u = T * pl.kp, t1u = t0u + pl.kp;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sum[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) sum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int sidx = seg; sidx < nseg; ++sidx) {
       const int a = piece_start(q, sidx), e = piece_start(q, sidx + 1);
       int which_slot;
       if (a >= t0u) which_slot = 0;       // the segment starts inside T
       else if (e > t0u) which_slot = 1;   // the leader, whose range ends inside T
       else break;
-      const f32x4 v = slots[(sidx * 2 + which_slot) * kWave + lane];
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) sum[e2] += v[e2];
+      for (int h = 0; h < NH; ++h) {
+        const f32x4 v = slots[((sidx * 2 + which_slot) * NH + h) * kWave + lane];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) sum[h][e2] += v[e2];
+      }
       if (e >= t1u) break;  // T ends in this segment
     }
-    store_tile<false>(s_rows, sum, sum, pl.m, pl.n, T * 16 + j, g);
+    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
   }
 }
 
@@ -1073,7 +1119,7 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
     pl.slots_off = need;
     need += slot_bytes + kCombineCounters;
   }
-  if (need < kCombineBytes) need = kCombineBytes;
+  if (need < slot_bytes) need = slot_bytes;
   const int fixed = table + kRowTableBytes;  // static LDS: decode table and row table
   pl.lds_bytes = need + fixed > kMinLds ? need : kMinLds - fixed;
   return pl;
@@ -1105,7 +1151,7 @@ std::map<int, DeviceState> g_dev;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 typedef void (*PrefillFn)(const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *, float *, uint32_t *,
-                          Plan, RowPtrs);
+                          float *, Plan, RowPtrs);
 template <bool TWO>
 PrefillFn prefill_fn_of(int v) {
   switch (v) {
@@ -1265,7 +1311,11 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
   Workspace *w = nullptr;
-  rc = workspace(stream, (size_t)pl.tiles * pl.panels * pl.maxc * 256 * (two ? 2 : 1), (size_t)pl.tiles, w);
+  // Partial slots, then (two matrices) one 2 KB slot per wave for the pair
+  // kept through the loop.
+  const size_t slot_floats = (size_t)pl.tiles * pl.panels * pl.maxc * 256 * (two ? 2 : 1);
+  const size_t kept_floats = two ? (size_t)pl.groups * pl.panels * kWaves * 512 : 0;
+  rc = workspace(stream, slot_floats + kept_floats, (size_t)pl.tiles, w);
   if (rc != TRELLIS_OK) return rc;
   RowPtrs rp{};
   pl.x_contiguous = 1;
@@ -1282,7 +1332,7 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
   hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, codes, scales_bf16, codes2, scales2, w->ws,
-                     w->counters, pl, rp);
+                     w->counters, w->ws + slot_floats, pl, rp);
   return launch_status();
 }
 
