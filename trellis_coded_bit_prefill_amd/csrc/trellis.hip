@@ -27,7 +27,10 @@
 //     rows that are never stored), B = W^T (16 rows);
 //   * tiles shared by pieces of one workgroup are summed through LDS, tiles
 //     shared with other workgroups through a workspace, in a fixed order
-//     either way, the last contributor (per-tile counter) writing bf16.
+//     either way, the last contributor (per-tile counter) writing bf16;
+//   * the fused gate/up variant decodes each block of both matrices against
+//     the same x into two accumulators, so the wave that completes a tile
+//     writes the elementwise tail itself.
 //
 // Build flags that matter for exactness: -ffp-contract=off.
 
