@@ -200,3 +200,26 @@ def test_prefill_packed_rejects_before_launch(lib):
     assert call_packed(g=tp.geom(17408, 5000, 4), xs=None) == tp.E_GEOMETRY
     with pytest.raises(ValueError):
         tp.prefill_packed_raw([FAKE], [0], FAKE, FAKE, tp.geom(**GOOD), [FAKE], 0)
+
+
+def test_one_hip_runtime_when_the_library_loads_before_torch():
+    # PyTorch-ROCm links its bundled HIP runtime by the plain name
+    # libamdhip64.so; the library links the runtime by its versioned name.
+    # The binding imports torch before loading the library, so a process
+    # that loads the library first still ends up with torch's runtime only
+    # (two runtimes: the library sees no device). A fresh interpreter checks
+    # the mapped files; no GPU is needed.
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import trellis_coded_bit_prefill_amd as tp\n"
+        "tp.load_library()\n"
+        "import torch\n"
+        "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n" % root
+    )
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

@@ -64,10 +64,21 @@ _lib = None
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libtrellis.so (raises OSError if it is not built)."""
+    """Load libtrellis.so (raises OSError if it is not built).
+
+    torch is imported first. PyTorch-ROCm ships its own HIP runtime and
+    links it by the plain name libamdhip64.so, while this library links the
+    runtime by its versioned name. Loaded first, the library would pull the
+    system runtime in, and torch would then load its own copy: two HIP
+    runtimes in one process, where the library finds no device and torch's
+    stream handles mean nothing to it. With torch loaded first, the library
+    binds to torch's runtime.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    import torch  # noqa: F401  (see the docstring)
+
     if not os.path.exists(path):
         raise OSError(f"{path} is not built; run trellis_coded_bit_prefill_amd/_build.py")
     L = ctypes.CDLL(path)
