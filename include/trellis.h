@@ -42,7 +42,9 @@
  *   NULL. The page's fixed K = 5120 is generalised to any multiple of 256.
  *
  * Execution: each call enqueues its work on `stream` (a hipStream_t; NULL is
- * the default stream) and returns without waiting. trellis_decode keeps no
+ * the default stream) and returns without waiting. The stream and every
+ * buffer must belong to the current device (hipGetDevice): the library sizes
+ * its launch and keeps its state for that device. trellis_decode keeps no
  * state. The other calls sum tiles that are split across workgroups
  * through a workspace (float32 partial tiles and per-tile counters) owned
  * by the library, one per (device, stream): it is allocated with hipMalloc on the first call

@@ -119,8 +119,12 @@ def _raise(status: int):
 
 
 def _stream_handle(device) -> int:
+    """The current stream of `device`, which must be the current device (the
+    library works on the current device)."""
     import torch
 
+    if device.index is not None and device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {device} but the current device is cuda:{torch.cuda.current_device()}")
     return torch.cuda.current_stream(device).cuda_stream
 
 
