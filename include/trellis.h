@@ -50,7 +50,10 @@
  * by the library, one per (device, stream): it is allocated with hipMalloc on the first call
  * that needs it, grown (never shrunk or freed) when a later call on that
  * stream needs more, and kept until the process exits; the kernel leaves
- * its counters at zero for the next call. Calls on different streams
+ * its counters at zero for the next call. A call that allocates cannot be
+ * captured into a HIP graph: make one call of the same shape on the stream
+ * before capturing it (the captured launches then reuse the workspace and
+ * may be replayed any number of times). Calls on different streams
  * therefore never share a workspace; calls on one stream are ordered by
  * the stream. Host-side state is guarded by a mutex, so calls
  * may come from several threads. Errors are returned, never thrown; a
