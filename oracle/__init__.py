@@ -74,6 +74,12 @@ def lib():
         L.oracle_prefill_rows.restype = None
         L.oracle_contract.argtypes = [u16p, c_int, u16p, c_int, c_int, f64p, f64p]
         L.oracle_contract.restype = None
+        L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_gate_up_chain.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.POINTER(c_int)]
+        L.oracle_gate_up_chain.restype = ctypes.c_uint16
+        L.oracle_gate_up_chain_n.argtypes = [u16p, u16p, ctypes.c_long, u16p, ctypes.POINTER(ctypes.c_uint8)]
+        L.oracle_gate_up_chain_n.restype = None
         _lib = L
     return _lib
 
@@ -182,6 +188,62 @@ def prefill(x, codes, scales, k: int, bits: int):
     return prefill_rows(x, codes, scales, k, bits, range(n))
 
 
+# ---- host-parallel drivers ---------------------------------------------------
+# The C functions run with the GIL released (ctypes), so contiguous row
+# ranges can go to a thread pool. Each thread computes whole output rows with
+# the same C code as above; the arithmetic per row is unchanged.
+
+def default_threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except (AttributeError, OSError):
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def _row_chunks(n: int, threads: int):
+    threads = max(1, min(threads, n))
+    step = -(-n // threads)
+    return [(r, min(n, r + step)) for r in range(0, n, step)]
+
+
+def decode_parallel(codes, scales, k: int, bits: int, threads: int | None = None):
+    """decode() with rows split over `threads` host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    codes, scales = _check(codes, scales, k, bits)
+    n = codes.shape[0]
+    w = np.empty((n, k), dtype=np.uint16)
+    chunks = _row_chunks(n, threads or default_threads())
+
+    def run(c):
+        r0, r1 = c
+        lib().oracle_decode_rows(_ptr(codes, ctypes.c_uint32), _ptr(scales, ctypes.c_uint16), k, bits, r0,
+                                 r1 - r0, _ptr(w[r0:r1], ctypes.c_uint16))
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        list(ex.map(run, chunks))
+    return w
+
+
+def prefill_parallel(x, codes, scales, k: int, bits: int, threads: int | None = None):
+    """prefill() (float64 y and sum |w*x| for every output row) with rows split
+    over `threads` host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    codes, scales = _check(codes, scales, k, bits)
+    n = codes.shape[0]
+    chunks = _row_chunks(n, threads or default_threads())
+    parts = [None] * len(chunks)
+
+    def run(i):
+        r0, r1 = chunks[i]
+        parts[i] = prefill_rows(x, codes, scales, k, bits, range(r0, r1))
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        list(ex.map(run, range(len(chunks))))
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
+
+
 def contract(x, w):
     """float64 y[M, N], a[M, N] from bf16 x[M, K] and an already decoded W[N, K]."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -228,6 +290,27 @@ def silu(g):
     g = np.asarray(g, dtype=np.float64)
     with np.errstate(over="ignore"):
         return g / (1.0 + np.exp(-g))
+
+
+def f64_to_bf16(v: float) -> int:
+    """bf16 bits of a float64 rounded to nearest even in one step."""
+    return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def gate_up_chain(gate_bf16, up_bf16):
+    """The page's bf16 chain on bf16 gate and up arrays (bit patterns):
+    h = bf16(bf16(gate * bf16(sigmoid(gate))) * up), each step exact and
+    rounded once. Returns (h bits, ambiguous), where ambiguous marks elements
+    whose exact sigmoid lies within 2^-21 (relative) of a bf16 rounding
+    boundary, so that a float32 sigmoid may legitimately round either way."""
+    g = np.ascontiguousarray(gate_bf16, dtype=np.uint16)
+    u = np.ascontiguousarray(up_bf16, dtype=np.uint16)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, dtype=np.uint16)
+    amb = np.empty(g.shape, dtype=np.uint8)
+    lib().oracle_gate_up_chain_n(_ptr(g, ctypes.c_uint16), _ptr(u, ctypes.c_uint16), g.size,
+                                 _ptr(h, ctypes.c_uint16), _ptr(amb, ctypes.c_uint8))
+    return h, amb.astype(bool)
 
 
 def gate_up_rows(x, codes_g, scales_g, codes_u, scales_u, k: int, bits: int, rows):

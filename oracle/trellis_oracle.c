@@ -168,3 +168,79 @@ void oracle_contract(const uint16_t *x, int m, const uint16_t *w, int k,
             a[(long)i * nrows + r] = sa;
         }
 }
+
+/* ---- gate/up tail of an MLP ---------------------------------------------
+ * Page "mlx-bun 0.0.4" (npm, page 62), section src/model/minicpm5.ts, MLP
+ * forward: the gate and up projections are bf16 arrays, and sigmoid(gate),
+ * gate * sigmoid(gate) and that product times up each yield a bf16 array.
+ * Here every step is taken exactly (float64 stands in for the exact real
+ * result: the products of two bf16 values are exact in it, and the sigmoid is
+ * accurate to about 1e-16 relative) and rounded once to bf16. */
+
+/* Round a double to bf16, to nearest, ties to even, in one step (no float32
+ * intermediate, so no double rounding). NaN maps to the quiet NaN 0x7FC0;
+ * values whose rounded magnitude reaches 2^128 become infinities. */
+uint16_t oracle_f64_to_bf16(double v) {
+    if (isnan(v))
+        return 0x7FC0u;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    int e;
+    (void)frexp(a, &e);             /* a = f * 2^e, 0.5 <= f < 1 */
+    int qexp = e - 8;               /* 8 significant bits: quantum 2^(e-8) */
+    if (qexp < -133)
+        qexp = -133;                /* bf16 subnormal quantum */
+    const double r = rint(ldexp(a, -qexp));   /* default mode: nearest, ties even */
+    const double res = ldexp(r, qexp);        /* a bf16 value, or >= 2^128 */
+    if (res >= 0x1p128)
+        return (uint16_t)(sign | 0x7F80u);
+    const float f = (float)res;                /* exact */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* 1 if the exact sigmoid of gate lies within 2^-21 (relative) of a point
+ * halfway between two bf16 values: there a float32 evaluation of the sigmoid,
+ * accurate to a few float32 ulps, may round to either neighbour. */
+static int near_bf16_midpoint(double s) {
+    const double a = fabs(s);
+    if (a == 0.0)
+        return 0;
+    int e;
+    (void)frexp(a, &e);
+    int qexp = e - 8;
+    if (qexp < -133)
+        qexp = -133;
+    const double scaled = ldexp(a, -qexp);
+    const double mid = floor(scaled) + 0.5;
+    return fabs(scaled - mid) * ldexp(1.0, qexp) <= a * 0x1p-21;
+}
+
+/* h = bf16(bf16(gate * bf16(sigmoid(gate))) * up) for bf16 gate and up.
+ * *ambiguous (if not NULL) is set when the sigmoid sits so close to a bf16
+ * rounding boundary that a float32 sigmoid may round the other way. */
+uint16_t oracle_gate_up_chain(uint16_t gate_bf16, uint16_t up_bf16, int *ambiguous) {
+    const double g = (double)oracle_bf16_to_f32(gate_bf16);
+    const double u = (double)oracle_bf16_to_f32(up_bf16);
+    const double sig_exact = 1.0 / (1.0 + exp(-g));
+    if (ambiguous)
+        *ambiguous = near_bf16_midpoint(sig_exact);
+    const double sig = (double)oracle_bf16_to_f32(oracle_f64_to_bf16(sig_exact));
+    const double silu = (double)oracle_bf16_to_f32(oracle_f64_to_bf16(g * sig));
+    return oracle_f64_to_bf16(silu * u);
+}
+
+/* Elementwise over n pairs. */
+void oracle_gate_up_chain_n(const uint16_t *gate, const uint16_t *up, long n, uint16_t *h, uint8_t *ambiguous) {
+    for (long i = 0; i < n; ++i) {
+        int amb = 0;
+        h[i] = oracle_gate_up_chain(gate[i], up[i], &amb);
+        if (ambiguous)
+            ambiguous[i] = (uint8_t)amb;
+    }
+}

@@ -1,10 +1,19 @@
 """GPU parity of trellis_gate_up against the CPU oracle.
 
 h = silu(x . Wg^T) * (x . Wu^T) with the page's bf16 roundings of every
-intermediate array. The reference is the exact float64 h = silu(g) * u of
-the float64 projections; the bound (oracle.gate_up_within_tolerance) carries
-the projections' tolerance through silu and the product and adds the chain's
-three bf16 roundings.
+intermediate array (page "mlx-bun 0.0.4" (npm, page 62), section
+src/model/minicpm5.ts, MLP forward). Two kinds of check:
+
+* one-hot x rows (a power of two at one column) make both projections a
+  single decoded weight times that power, exact in any summation order, so h
+  has one right answer: the oracle's bf16 chain (oracle.gate_up_chain) on
+  those two bf16 values. The device must match it bit for bit, except where
+  the exact sigmoid sits within 2^-21 of a bf16 rounding boundary (a float32
+  sigmoid may round either way there); those are counted and must be rare.
+* general x: the exact float64 h = silu(g) * u of the float64 projections,
+  with a bound (oracle.gate_up_within_tolerance) that carries the
+  projections' tolerance through silu and the product and adds the chain's
+  three bf16 roundings.
 """
 import numpy as np
 import pytest
@@ -98,6 +107,39 @@ def test_gate_up_barrier_combine(bits, m, n):
         rng = np.random.default_rng(17)
         rows = np.unique(np.concatenate([np.arange(48), np.arange(n - 48, n), rng.integers(0, n, 320)]))
     check(h, x, cg, sg, cu, su, k, bits, rows, f"barrier combine m={m} n={n} bits={bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("m", [1, 5, 15])
+def test_gate_up_one_hot_bit_exact_chain(bits, m):
+    # n spans many tiles and a ragged tail; k has four blocks. Row i of x is
+    # 2^p_i at column j_i, so gate[i, n] = 2^p_i * Wg[n, j_i] exactly (and up
+    # likewise): gates from about 1e-4 to 16 cover the sigmoid's curved part.
+    n, k = 2004, 1024
+    print(f"gate_up one-hot m={m} bits={bits}", flush=True)
+    _, cg, sg = generate(5, k, n, bits, seed=9400 + bits)
+    _, cu, su = generate(5, k, n, bits, seed=9500 + bits)
+    rng = np.random.default_rng(9600 + 16 * bits + m)
+    cols = rng.choice(k, size=m, replace=False)
+    pows = np.array([0, 2, 4, 6, 8, 1, 3, 5, 7, 0, 2, 4, 6, 8, 5])[:m]
+    x = np.zeros((m, k), dtype=np.uint16)
+    x[np.arange(m), cols] = (0x3F80 + (pows << 7)).astype(np.uint16)   # 2^p as bf16
+    h = gpu_gate_up(x, cg, sg, cu, su, bits)
+    wg = oracle.decode(cg, sg, k, bits)[:, cols].T      # [m, n] bf16 bits
+    wu = oracle.decode(cu, su, k, bits)[:, cols].T
+    # 2^p * w in bf16: add p to the exponent field of every nonzero weight
+    def scaled(w):
+        w = w.astype(np.uint32)
+        nz = (w & 0x7FFF) != 0
+        return np.where(nz, w + (pows[:, None].astype(np.uint32) << 7), w).astype(np.uint16)
+    want, amb = oracle.gate_up_chain(scaled(wg), scaled(wu))
+    same = (h == want) | (((h & 0x7FFF) == 0) & ((want & 0x7FFF) == 0))
+    bad = ~same & ~amb
+    assert not bad.any(), (f"{int(bad.sum())} of {h.size} differ from the chain; first "
+                           f"{[(int(i), int(j), hex(h[i, j]), hex(want[i, j])) for i, j in np.argwhere(bad)[:4]]}")
+    assert amb.sum() <= max(10, h.size // 100), int(amb.sum())
+    print(f"  {int(amb.sum())} of {h.size} sigmoids next to a bf16 boundary; "
+          f"{int((~same & amb).sum())} of them rounded the other way", flush=True)
 
 
 def test_gate_up_deterministic():

@@ -447,3 +447,129 @@ def test_gate_up_tolerance_accepts_the_chain_and_rejects_a_slip():
     sel = (g >= 0.5) & (np.abs(h) > 0.5)
     assert sel.sum() > 100
     assert not oracle.gate_up_within_tolerance(far, h, g, np.zeros_like(ag), u, np.zeros_like(au))[sel].any()
+
+
+# ---- bf16 chain of the gate/up tail ------------------------------------------
+# Page "mlx-bun 0.0.4" (npm, page 62), section src/model/minicpm5.ts, MLP
+# forward: sigmoid(gate), gate * sigmoid(gate) and that times up are each a
+# bf16 array. oracle.gate_up_chain rounds each exact step once; it is pinned
+# here against exact rational rounding and a 40-digit decimal sigmoid.
+
+def _bf16_round_fraction(q: Fraction) -> int:
+    """bf16 bits of the exact rational q, to nearest, ties to even (integer
+    arithmetic on q's numerator and denominator; finite, |q| < 2^128)."""
+    if q == 0:
+        return 0
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    num, den = a.numerator, a.denominator
+    e = num.bit_length() - den.bit_length()          # 2^e <= a < 2^(e+2)
+    if Fraction(num, den) < Fraction(2) ** e:
+        e -= 1
+    if Fraction(num, den) >= Fraction(2) ** (e + 1):
+        e += 1
+    qexp = max(e - 7, -133)                            # quantum of a's binade
+    scaled = a / (Fraction(2) ** qexp)
+    r, rem = divmod(scaled.numerator, scaled.denominator)
+    twice = 2 * rem
+    if twice > scaled.denominator or (twice == scaled.denominator and r & 1):
+        r += 1
+    val = Fraction(r) * Fraction(2) ** qexp
+    bits = int(np.array([float(val)], dtype=np.float32).view(np.uint32)[0]) >> 16
+    return sign | bits
+
+
+def test_f64_to_bf16_is_exact_single_rounding():
+    rng = np.random.default_rng(41)
+    vals = list(rng.normal(0, 1, 3000) * np.exp2(rng.integers(-140, 127, 3000)))
+    # exact midpoints between neighbouring bf16 values and their f64 neighbours
+    for b in rng.integers(0x0001, 0x7F7F, 600):
+        lo = float(bf16_value([b])[0])
+        hi = float(bf16_value([b + 1])[0])
+        mid = (lo + hi) / 2
+        vals += [mid, np.nextafter(mid, 0.0), np.nextafter(mid, np.inf), -mid]
+    for v in vals:
+        want = _bf16_round_fraction(Fraction(float(v)))
+        got = oracle.f64_to_bf16(float(v))
+        assert got == want, (v, hex(got), hex(want))
+    # a value one float32 rounding would push onto a tie: 1 + 2^-8 + 2^-40
+    # rounds up in one step (and to even, down, after a float32 rounding)
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle.f64_to_bf16(float(np.float32(1.0 + 2.0 ** -8 + 2.0 ** -40))) == 0x3F80
+
+
+def _chain_reference(gate_bits: int, up_bits: int, drop: str = ""):
+    """The page's chain with a 40-digit decimal sigmoid and exact rational
+    products; `drop` skips one rounding ("sig" or "silu") for the negative
+    controls below."""
+    from decimal import Decimal, localcontext
+
+    g = Fraction(float(bf16_value([gate_bits])[0]))
+    u = Fraction(float(bf16_value([up_bits])[0]))
+    with localcontext() as ctx:
+        ctx.prec = 40
+        ctx.Emax = 10 ** 6
+        ctx.Emin = -10 ** 6
+        dg = Decimal(g.numerator) / Decimal(g.denominator)
+        sig = Fraction(Decimal(1) / (Decimal(1) + (-dg).exp()))
+    sig_r = sig if drop == "sig" else Fraction(float(bf16_value([_bf16_round_fraction(sig)])[0]))
+    silu = g * sig_r
+    silu_r = silu if drop == "silu" else Fraction(float(bf16_value([_bf16_round_fraction(silu)])[0]))
+    return _bf16_round_fraction(silu_r * u)
+
+
+def test_gate_up_chain_exhaustive_gates_against_decimal():
+    # every bf16 gate with |gate| < 2^11 (beyond that sigmoid is 0 or 1 in
+    # every format) against one up with a full 8-bit significand, so the
+    # final rounding is exercised too
+    gates = np.array([b for b in range(0x10000) if (b & 0x7FFF) < 0x4500], dtype=np.uint16)
+    up = np.full(gates.shape, 0xBFB5, dtype=np.uint16)   # -1.4140625
+    h, amb = oracle.gate_up_chain(gates, up)
+    want = np.array([_chain_reference(int(g), 0xBFB5) for g in gates], dtype=np.uint16)
+    same = (h == want) | ((h & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+    assert same.all(), [(hex(g), hex(a), hex(b)) for g, a, b in zip(gates[~same][:5], h[~same][:5], want[~same][:5])]
+    # the ambiguity flag is rare (sigmoid within 2^-21 of a bf16 midpoint)
+    assert amb.sum() < 40
+
+
+def test_gate_up_chain_closed_forms():
+    one, two, zero = 0x3F80, 0x4000, 0x0000
+    # gate = 0: sigmoid 1/2, silu 0, h = 0
+    h, _ = oracle.gate_up_chain(np.array([zero], np.uint16), np.array([two], np.uint16))
+    assert (h[0] & 0x7FFF) == 0
+    # gate = ln 3 rounded: sigmoid close to 3/4 -> bf16 0.75 exactly when the
+    # rounded gate keeps the sigmoid within half an ulp of 0.75
+    g = oracle.f64_to_bf16(np.log(3.0))
+    gv = float(bf16_value([g])[0])
+    s = 1 / (1 + np.exp(-gv))
+    assert abs(s - 0.75) < 2 ** -10
+    h, _ = oracle.gate_up_chain(np.array([g], np.uint16), np.array([one], np.uint16))
+    assert h[0] == oracle.f64_to_bf16(gv * 0.75)
+    # large gates: sigmoid rounds to 1 (gate >= 2^4 is enough) so h = bf16(gate*up)
+    big = np.array([0x4180, 0x4200, 0x4380], np.uint16)     # 16, 32, 256
+    upv = np.array([0x3FB5, 0xC0A1, 0x3E01], np.uint16)
+    h, _ = oracle.gate_up_chain(big, upv)
+    for i in range(3):
+        gv = float(bf16_value([big[i]])[0])
+        uv = float(bf16_value([upv[i]])[0])
+        assert h[i] == oracle.f64_to_bf16(gv * uv)
+    # very negative gates: silu underflows to (-)0
+    h, _ = oracle.gate_up_chain(np.array([0xC400, 0xC2C8], np.uint16), np.array([one, one], np.uint16))
+    assert ((h & 0x7FFF) == 0).all()
+
+
+@pytest.mark.parametrize("drop", ["sig", "silu"])
+def test_gate_up_chain_each_rounding_is_observable(drop):
+    # One-hot x turns the device's gate and up into single decoded weights
+    # times a power of two, so a bit-exact comparison against the chain sees
+    # any missing rounding: on gates and ups of that kind, dropping the
+    # rounding of sigmoid(gate) or of gate * sigmoid(gate) changes a sizeable
+    # share of the outputs.
+    rng = np.random.default_rng(53)
+    w = rng.normal(0, 0.02, 1500).astype(np.float32)
+    p = np.exp2(rng.integers(0, 9, 1500)).astype(np.float32)
+    gates = torch_bf16_bits(w * p)
+    ups = torch_bf16_bits(rng.normal(0, 0.02, 1500).astype(np.float32) * 16)
+    h, _ = oracle.gate_up_chain(gates, ups)
+    diff = sum(int(h[i]) != _chain_reference(int(gates[i]), int(ups[i]), drop) for i in range(len(gates)))
+    assert diff > 100, diff
