@@ -46,24 +46,31 @@
  * buffer must belong to the current device (hipGetDevice): the library sizes
  * its launch and keeps its state for that device. trellis_decode keeps no
  * state. The other calls sum tiles that are split across workgroups
- * through a workspace (float32 partial tiles and per-tile counters) owned
- * by the library, one per (device, stream): it is allocated with hipMalloc on the first call
- * that needs it, grown (never shrunk or freed) when a later call on that
- * stream needs more, and kept until the process exits; the kernel leaves
- * its counters at zero for the next call. A call that allocates cannot be
- * captured into a HIP graph: make one call of the same shape on the stream
- * before capturing it (the captured launches then reuse the workspace and
- * may be replayed any number of times). Calls on different streams
- * therefore never share a workspace; calls on one stream are ordered by
- * the stream. Host-side state is guarded by a mutex, so calls
- * may come from several threads. Errors are returned, never thrown; a
- * validation error leaves every output untouched.
+ * through a workspace (float32 partial tiles and per-tile counters that the
+ * kernel leaves at zero for the next call) owned by the library, one per
+ * (device, stream) -- and, for the per-thread default stream
+ * hipStreamPerThread, one per calling host thread as well. It is allocated
+ * with hipMalloc on the first call that needs it, grown when a later call
+ * needs more (the outgrown buffer is not freed: queued launches and captured
+ * graphs may hold its address) and kept until the process exits.
+ * Consequences:
+ *   - calls on one stream are ordered by the stream and share its workspace
+ *     safely; calls on different streams use different workspaces;
+ *   - a call that allocates cannot be captured into a HIP graph: make one
+ *     call of the same shape on the stream before capturing it;
+ *   - a captured launch keeps the capture stream's workspace. Replay the
+ *     graph on the capture stream, or on a stream ordered with every other
+ *     use of the capture stream's workspace: a replay that overlaps an
+ *     eager call (or another replay) on the capture stream races on the
+ *     same counters and partial tiles and can give wrong results.
+ * Host-side state is guarded by a mutex, so calls may come from several
+ * threads. Errors are returned, never thrown; a validation error leaves every
+ * output untouched.
  *
  * Decode table: the library picks, per call, the LDS table that lets the
  * most of x stay in one K panel (a window -> value table, a window ->
- * float16 code table, or for k = 2 a table of code pairs). The environment
- * variable TRELLIS_TABLE = value | code | pair forces one (for testing and
- * tuning; pair only for k = 2); every table gives the same weights.
+ * float16 code table, or for k = 2 a table of code pairs); every table gives
+ * the same weights. trellis_testing.h has a hook that forces one, for tests.
  */
 #ifndef TRELLIS_H
 #define TRELLIS_H

@@ -18,3 +18,13 @@ def oracle_lib():
 
     oracle.lib()
     return oracle
+
+
+@pytest.fixture
+def force_table():
+    """Setter for the library's decode-table test hook; the library's own
+    choice is restored when the test ends."""
+    import trellis_coded_bit_prefill_amd as tp
+
+    yield tp.force_table
+    tp.force_table(None)

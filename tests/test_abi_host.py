@@ -11,9 +11,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "trellis.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(trellis_[a-z_]+)\s*\(", src)))
+    """Every function declared in include/*.h."""
+    import glob
+
+    names = set()
+    for path in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(trellis_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +31,16 @@ def lib():
 
 
 def test_header_declares_the_bound_functions():
-    assert declared_functions() == sorted(tp.EXPORTED)
+    assert declared_functions() == sorted(tp.EXPORTED + tp.EXPORTED_TESTING)
+
+
+def test_table_hook_round_trips(lib):
+    assert tp.force_table("code") is None
+    assert tp.force_table("pair") == "code"
+    assert tp.force_table(None) == "pair"
+    assert lib.trellis_test_force_table(7) == -2
+    assert lib.trellis_test_force_table(-3) == -2
+    assert tp.force_table(None) is None
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -131,7 +131,7 @@ def test_prefill_k_panels_with_whole_tiles_per_wave():
 
 @pytest.mark.parametrize("bits,shift,table", [(2, 0, "pair"), (2, 1, "pair"), (2, 0, "value"), (2, 0, "code"),
                                               (3, 0, "value"), (3, 0, "code"), (4, 0, "value"), (4, 0, "code")])
-def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift, table, monkeypatch):
+def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift, table, force_table):
     # One-hot x rows pick single columns of W, so every output is one decoded
     # weight (sum of one exact product): prefill's in-kernel decode (the LDS
     # table named by `table` and the ALU path) must give exactly the oracle's
@@ -142,7 +142,7 @@ def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift, table, mo
     # pair-table entry.
     import torch
 
-    monkeypatch.setenv("TRELLIS_TABLE", table)
+    force_table(table)
     print(f"prefill one-hot exhaustive bits={bits} shift={shift} table={table}", flush=True)
     rng = np.random.default_rng(600 + bits + 10 * shift)
     extra = [0x3F80, 0xBF80, 0xBC00, 0xBCA4, 0x0000, 0x8000, 0x0B00, 0x7300, 0x3FFF, 0xC07F,
@@ -169,11 +169,11 @@ def test_prefill_weights_bit_exact_every_window_and_scale(bits, shift, table, mo
 @pytest.mark.parametrize("bits,table", [(2, "value"), (2, "code"), (2, "pair"), (3, "value"), (3, "code"),
                                         (4, "value"), (4, "code")])
 @pytest.mark.parametrize("m,k", [(5, 1280), (15, 5120)])
-def test_prefill_each_table(bits, table, m, k, monkeypatch):
+def test_prefill_each_table(bits, table, m, k, force_table):
     # Every decode table on one shape with several tiles and a ragged last
     # tile; M = 15, K = 5120 needs two K panels with the value or pair table
     # and one with the code table.
-    monkeypatch.setenv("TRELLIS_TABLE", table)
+    force_table(table)
     n = 84
     print(f"prefill table={table} m={m} k={k} n={n} bits={bits}", flush=True)
     x, codes, scales = generate(m, k, n, bits, seed=5000 + 3 * m + bits)

@@ -65,14 +65,14 @@ def need_gpu():
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}-k{c[2]}-{c[3] or 'auto'}-m{c[4]}-K{c[5]}-N{c[6]}")
-def test_sweep(case, monkeypatch):
+def test_sweep(case, force_table):
     import torch
 
     i, entry, bits, table, m, k, n, groups, seed = case
     if table is not None:
-        monkeypatch.setenv("TRELLIS_TABLE", table)
+        force_table(table)
     else:
-        monkeypatch.delenv("TRELLIS_TABLE", raising=False)
+        force_table(None)
     what = f"sweep case {i}: {entry} bits={bits} table={table} m={m} k={k} n={n} groups={groups} seed={seed}"
     print(what, flush=True)
     if entry in ("prefill", "matvec"):

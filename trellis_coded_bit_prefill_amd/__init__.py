@@ -37,6 +37,9 @@ E_HIP = -5
 # Every symbol declared in include/trellis.h.
 EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_prefill_packed",
             "trellis_gate_up", "trellis_status_string")
+# Test and tuning hooks (include/trellis_testing.h).
+EXPORTED_TESTING = ("trellis_test_force_table",)
+TABLES = {"value": 0, "code": 1, "pair": 2}
 
 
 class Geom(ctypes.Structure):
@@ -97,8 +100,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_prefill_packed.restype = ctypes.c_int
     L.trellis_gate_up.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, Geom, vp, vp]
     L.trellis_gate_up.restype = ctypes.c_int
+    L.trellis_test_force_table.argtypes = [ctypes.c_int]
+    L.trellis_test_force_table.restype = ctypes.c_int
     _lib = L
     return L
+
+
+def force_table(name):
+    """Test hook: force the decode table of later calls ("value", "code",
+    "pair" (k = 2 only) or None for the library's choice). Returns the
+    previous setting's name."""
+    kind = -1 if name is None else TABLES[name]
+    prev = load_library().trellis_test_force_table(kind)
+    if prev < -1:
+        raise ValueError(f"bad table {name!r}")
+    return None if prev == -1 else {v: k for k, v in TABLES.items()}[prev]
 
 
 def status_string(status: int) -> str:

@@ -37,15 +37,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <map>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <thread>
 #include <utility>
 #include <vector>
 
 #include "decode.hpp"
 #include "trellis.h"
+#include "trellis_testing.h"
 
 namespace trellis {
 namespace {
@@ -1151,7 +1154,20 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Workspaces are keyed by device and stream; the per-thread default stream is
+// one handle for many streams (one per host thread), so its key also holds
+// the calling thread.
+struct WsKey {
+  int dev;
+  hipStream_t stream;
+  std::thread::id thread;
+  bool operator<(const WsKey &o) const {
+    if (dev != o.dev) return dev < o.dev;
+    if (stream != o.stream) return stream < o.stream;
+    return thread < o.thread;
+  }
+};
+std::map<WsKey, Workspace> g_ws;
 
 typedef void (*PrefillFn)(const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *, float *, uint32_t *,
                           float *, Plan, RowPtrs);
@@ -1188,12 +1204,14 @@ trellis_status device_state(DeviceState *&st, int v) {
 }
 
 // Per (device, stream) workspace: partial tiles and self-resetting counters.
-// Grown on demand and kept until process exit; a grown-out buffer is not
-// freed because earlier launches on the stream may still be using it.
+// Grown on demand and kept until process exit. A grown-out buffer is not
+// freed: launches still queued on the stream, and HIP graphs captured from
+// earlier calls, hold its address.
 trellis_status workspace(hipStream_t stream, size_t ws_floats, size_t ncounters, Workspace *&out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
-  Workspace &w = g_ws[{dev, stream}];
+  const std::thread::id tid = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+  Workspace &w = g_ws[WsKey{dev, stream, tid}];
   if (w.ws_floats < ws_floats) {
     float *p = nullptr;
     if (hipMalloc(&p, ws_floats * sizeof(float)) != hipSuccess) return TRELLIS_E_HIP;
@@ -1260,15 +1278,15 @@ trellis_status trellis_decode(const uint32_t *codes, const uint16_t *scales_bf16
 namespace trellis {
 namespace {
 
-// TRELLIS_TABLE=value|code|pair in the environment forces the decode table
-// (testing and tuning); pair applies to k = 2 only. -1: no override.
+// Decode-table override for tests and tuning (trellis_test_force_table):
+// -1 lets the library choose; value/code/pair force that table (pair applies
+// to k = 2 only). One relaxed atomic load per call, no environment lookup.
+std::atomic<int> g_force_table{-1};
+
 int table_override(int bits) {
-  const char *e = std::getenv("TRELLIS_TABLE");
-  if (!e) return -1;
-  if (!std::strcmp(e, "value")) return kValueTable;
-  if (!std::strcmp(e, "code")) return kCodeTable;
-  if (!std::strcmp(e, "pair") && bits == 2) return kPairTable;
-  return -1;
+  const int t = g_force_table.load(std::memory_order_relaxed);
+  if (t == kPairTable && bits != 2) return -1;
+  return t;
 }
 
 // One launch of the layer on m <= 15 rows (any m >= 1 with a valid
@@ -1415,6 +1433,11 @@ trellis_status trellis_prefill_packed(const uint16_t *const *x_groups, const int
   }
   if (n > 0) return launch_rows(xr, orow, n, codes, scales_bf16, nullptr, nullptr, g, stream);
   return TRELLIS_OK;
+}
+
+int trellis_test_force_table(int kind) {
+  if (kind < -1 || kind > 2) return -2;
+  return g_force_table.exchange(kind);
 }
 
 trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m, const uint32_t *codes_gate,
