@@ -90,6 +90,9 @@ extern "C" {
 #define TRELLIS_MAX_N (1 << 22)
 #define TRELLIS_MAX_GROUPS 4096
 #define TRELLIS_MAX_GROUP_ROWS (1 << 20)
+/* Device memory of trellis_prefill_noalloc, per GPU: 1 MiB of tile counters
+ * plus 31 MiB of float32 partial tiles. */
+#define TRELLIS_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Geometry of one packed linear layer: n output rows (out features), k input
  * columns (in features), block length t (must be 256), window length l (must
@@ -108,7 +111,8 @@ typedef enum trellis_status {
     TRELLIS_E_M = -2,        /* m outside [5, 15] (prefill) or [1, 4] (matvec); bad packed group or row counts */
     TRELLIS_E_NULL = -3,     /* a required pointer is NULL */
     TRELLIS_E_ALIGN = -4,    /* a pointer is not aligned as documented */
-    TRELLIS_E_HIP = -5       /* the HIP runtime reported a launch error */
+    TRELLIS_E_HIP = -5,      /* the HIP runtime reported a launch error */
+    TRELLIS_E_SCRATCH = -6   /* trellis_prefill_noalloc: the call's workspace exceeds the fixed scratch */
 } trellis_status;
 
 /* 1 if (g, m) is inside the accepted domain of trellis_prefill, else 0.
@@ -184,6 +188,25 @@ trellis_status trellis_gate_up(const uint16_t *x_bf16, int32_t m,
                                const uint32_t *codes_gate, const uint16_t *scales_gate,
                                const uint32_t *codes_up, const uint16_t *scales_up,
                                trellis_geom g, uint16_t *h_bf16, void *hip_stream);
+
+/* trellis_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, formats, tolerance and kernels, but the workspace is a
+ * fixed array of TRELLIS_NOALLOC_SCRATCH_BYTES in the library's device image
+ * (one per GPU, held until the process ends) instead of memory the library
+ * allocates. The call itself allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine. Its first call on a GPU looks up that GPU's
+ * copy of the array and clears its counter region with a kernel on `stream`.
+ * Limit: the partial tiles must fit in 31 MiB -- about
+ * ceil(N/16) * (K panels) * (contributors per tile) KiB; every shape with
+ * N <= 65536 at K = 5120 (and the K = 17408, N = 5120 down projection) fits.
+ * Larger calls return TRELLIS_E_SCRATCH before any GPU work. All calls on
+ * one GPU share its array, whatever their stream: calls that overlap in time
+ * on one GPU race on it and can give wrong results, so the caller must order
+ * them (one stream, or events). */
+trellis_status trellis_prefill_noalloc(const uint16_t *x_bf16, int32_t m,
+                                       const uint32_t *codes, const uint16_t *scales_bf16,
+                                       trellis_geom g, uint16_t *out_bf16, void *hip_stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *trellis_status_string(trellis_status s);

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in (tp.OK, tp.E_GEOMETRY, tp.E_M, tp.E_NULL, tp.E_ALIGN, tp.E_HIP):
+    for s in (tp.OK, tp.E_GEOMETRY, tp.E_M, tp.E_NULL, tp.E_ALIGN, tp.E_HIP, tp.E_SCRATCH):
         assert tp.status_string(s)
     assert tp.status_string(123) == "unknown status"
 

@@ -33,10 +33,12 @@ E_M = -2
 E_NULL = -3
 E_ALIGN = -4
 E_HIP = -5
+E_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol declared in include/trellis.h.
 EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_prefill_packed",
-            "trellis_gate_up", "trellis_status_string")
+            "trellis_gate_up", "trellis_prefill_noalloc", "trellis_status_string")
 # Test and tuning hooks (include/trellis_testing.h).
 EXPORTED_TESTING = ("trellis_test_force_table",)
 TABLES = {"value": 0, "code": 1, "pair": 2}
@@ -100,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_prefill_packed.restype = ctypes.c_int
     L.trellis_gate_up.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, Geom, vp, vp]
     L.trellis_gate_up.restype = ctypes.c_int
+    L.trellis_prefill_noalloc.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
+    L.trellis_prefill_noalloc.restype = ctypes.c_int
     L.trellis_test_force_table.argtypes = [ctypes.c_int]
     L.trellis_test_force_table.restype = ctypes.c_int
     _lib = L
@@ -179,6 +183,12 @@ def prefill_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, ou
     _raise(load_library().trellis_prefill(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
 
 
+def prefill_noalloc_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out_ptr: int,
+                        stream: int) -> None:
+    """Direct C-ABI call of the no-allocation variant (fixed device scratch)."""
+    _raise(load_library().trellis_prefill_noalloc(x_ptr, m, codes_ptr, scales_ptr, g, out_ptr, stream))
+
+
 def matvec_raw(x_ptr: int, m: int, codes_ptr: int, scales_ptr: int, g: Geom, out_ptr: int,
                stream: int) -> None:
     """Direct C-ABI call with raw device addresses (1 <= m <= 4)."""
@@ -245,6 +255,13 @@ def prefill(x, codes, scales, bits: int, out=None):
     """out[M, N] = x[M, K] . W^T (bf16), W decoded on the fly, current stream
     (5 <= M <= 15)."""
     return _linear(prefill_raw, x, codes, scales, bits, out)
+
+
+def prefill_noalloc(x, codes, scales, bits: int, out):
+    """prefill() without any device allocation by the library: `out` must be
+    given, and the workspace is the library's fixed per-GPU scratch (calls on
+    one GPU must not overlap)."""
+    return _linear(prefill_noalloc_raw, x, codes, scales, bits, out)
 
 
 def matvec(x, codes, scales, bits: int, out=None):

@@ -1045,6 +1045,16 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   }
 }
 
+// Device memory of trellis_prefill_noalloc (callers that cannot allocate): a
+// fixed region of per-tile counters (one per tile of the largest accepted N),
+// then the float32 partial tiles. One copy per device, held until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kScratchBytes = (size_t)TRELLIS_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCounterBytes = (size_t)(TRELLIS_MAX_N / 16) * 4;
+static_assert(kScratchCounterBytes % 256 == 0 && kScratchCounterBytes < kScratchBytes, "scratch layout");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -1143,7 +1153,11 @@ constexpr int variant_table(int v) { return v % kTables == kVariantPair ? kPairT
 struct DeviceState {
   int cus = 0;
   bool lds_attr_set[kVariants] = {};
+  // trellis_prefill_noalloc: this device's address of `scratch` (0 until the
+  // first such call on the device) and whether its counters were cleared.
+  unsigned char *scratch = nullptr;
 };
+constexpr int kMaxDevices = 64;
 
 struct Workspace {
   float *ws = nullptr;
@@ -1153,7 +1167,7 @@ struct Workspace {
 };
 
 std::mutex g_mu;
-std::map<int, DeviceState> g_dev;
+DeviceState g_dev[kMaxDevices];  // fixed: looking a device up allocates nothing
 // Workspaces are keyed by device and stream; the per-thread default stream is
 // one handle for many streams (one per host thread), so its key also holds
 // the calling thread.
@@ -1187,7 +1201,7 @@ PrefillFn prefill_fn(int v) { return v >= kTables ? prefill_fn_of<true>(v - kTab
 
 trellis_status device_state(DeviceState *&st, int v) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TRELLIS_E_HIP;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRELLIS_E_HIP;
   DeviceState &d = g_dev[dev];
   if (d.cus == 0) {
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || d.cus <= 0)
@@ -1252,6 +1266,7 @@ const char *trellis_status_string(trellis_status s) {
     case TRELLIS_E_NULL: return "null pointer argument";
     case TRELLIS_E_ALIGN: return "misaligned pointer argument";
     case TRELLIS_E_HIP: return "HIP runtime error";
+    case TRELLIS_E_SCRATCH: return "the call needs more workspace than the no-allocation entry point's fixed scratch holds";
   }
   return "unknown status";
 }
@@ -1294,9 +1309,12 @@ int table_override(int bits) {
 // x_rows[i], output row i at out_rows[i]. With a second matrix (codes2,
 // scales2, the up projection) the output is the elementwise tail of the
 // two projections, from the same launch.
+// noalloc: the workspace is this device's `scratch` array instead of the
+// stream's allocated workspace; a call whose workspace would not fit returns
+// TRELLIS_E_SCRATCH before any GPU work.
 trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_rows, int32_t m,
                            const uint32_t *codes, const uint16_t *scales_bf16, const uint32_t *codes2,
-                           const uint16_t *scales2, trellis_geom g, hipStream_t stream) {
+                           const uint16_t *scales2, trellis_geom g, hipStream_t stream, bool noalloc = false) {
   const bool two = codes2 != nullptr;
   int cus = 0;
   {
@@ -1331,13 +1349,25 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   DeviceState *st = nullptr;
   trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
-  Workspace *w = nullptr;
   // Partial slots, then (two matrices) one 2 KB slot per wave for the pair
   // kept through the loop.
   const size_t slot_floats = (size_t)pl.tiles * pl.panels * pl.maxc * 256 * (two ? 2 : 1);
   const size_t kept_floats = two ? (size_t)pl.groups * pl.panels * kWaves * 512 : 0;
-  rc = workspace(stream, slot_floats + kept_floats, (size_t)pl.tiles, w);
-  if (rc != TRELLIS_OK) return rc;
+  float *ws = nullptr;
+  uint32_t *counters = nullptr;
+  if (noalloc) {
+    // Counters (zero between calls: the kernel resets each one it uses, and
+    // the first call on the device cleared them all), then the partial slots.
+    if (two || (slot_floats + kept_floats) * 4 > kScratchBytes - kScratchCounterBytes) return TRELLIS_E_SCRATCH;
+    counters = reinterpret_cast<uint32_t *>(st->scratch);
+    ws = reinterpret_cast<float *>(st->scratch + kScratchCounterBytes);
+  } else {
+    Workspace *w = nullptr;
+    rc = workspace(stream, slot_floats + kept_floats, (size_t)pl.tiles, w);
+    if (rc != TRELLIS_OK) return rc;
+    ws = w->ws;
+    counters = w->counters;
+  }
   RowPtrs rp{};
   pl.x_contiguous = 1;
   for (int i = 0; i < m; ++i) {
@@ -1352,8 +1382,8 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
   }
   const dim3 grid((unsigned)(pl.groups * pl.panels)), block(kWgThreads);
   clear_last_error();
-  hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, codes, scales_bf16, codes2, scales2, w->ws,
-                     w->counters, w->ws + slot_floats, pl, rp);
+  hipLaunchKernelGGL(prefill_fn(v), grid, block, pl.lds_bytes, stream, codes, scales_bf16, codes2, scales2, ws,
+                     counters, ws + slot_floats, pl, rp);
   return launch_status();
 }
 
@@ -1433,6 +1463,43 @@ trellis_status trellis_prefill_packed(const uint16_t *const *x_groups, const int
   }
   if (n > 0) return launch_rows(xr, orow, n, codes, scales_bf16, nullptr, nullptr, g, stream);
   return TRELLIS_OK;
+}
+
+trellis_status trellis_prefill_noalloc(const uint16_t *x_bf16, int32_t m, const uint32_t *codes,
+                                       const uint16_t *scales_bf16, trellis_geom g, uint16_t *out_bf16,
+                                       void *hip_stream) {
+  if (!geometry_ok(g)) return TRELLIS_E_GEOMETRY;
+  if (m < TRELLIS_MIN_M || m > TRELLIS_MAX_M) return TRELLIS_E_M;
+  if (!x_bf16 || !codes || !scales_bf16 || !out_bf16) return TRELLIS_E_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(out_bf16, 16) || !aligned(scales_bf16, 2))
+    return TRELLIS_E_ALIGN;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  // Set-up, once per device with that device current: the device's own
+  // address of `scratch` (the array's name is only a host-side stand-in),
+  // and the counter region cleared by a kernel on the caller's stream, so it
+  // is ordered before this call's launch (and, calls on one device being
+  // serialised by the caller, before every later call).
+  DeviceState *st = nullptr;
+  trellis_status rc = device_state(st, variant_of(g.bits, kValueTable, false));
+  if (rc != TRELLIS_OK) return rc;
+  if (!st->scratch) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TRELLIS_E_HIP;
+    const int64_t n = (int64_t)(kScratchCounterBytes / 4);
+    clear_last_error();
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t *>(p), n);
+    if (hipGetLastError() != hipSuccess) return TRELLIS_E_HIP;
+    st->scratch = static_cast<unsigned char *>(p);
+  }
+  const uint16_t *xr[kMaxRows];
+  uint16_t *orow[kMaxRows];
+  for (int i = 0; i < m; ++i) {
+    xr[i] = x_bf16 + (size_t)i * g.k;
+    orow[i] = out_bf16 + (size_t)i * g.n;
+  }
+  return launch_rows(xr, orow, m, codes, scales_bf16, nullptr, nullptr, g, stream, true);
 }
 
 int trellis_test_force_table(int kind) {
