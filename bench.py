@@ -273,8 +273,6 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' figures")
     ap.add_argument("--extra-steps", type=int, default=300,
                     help="timed steps per extra workload (after as many warm-up steps)")
-    ap.add_argument("--contraction", choices=("mfma", "valu"), default="mfma",
-                    help="valu: the VALU-dot measurement variant where it exists (k = 4, M = 5 or 1)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -305,9 +303,6 @@ def main():
     torch.cuda.set_device(dev)
     tp.load_library()
 
-    if args.contraction == "valu":
-        tp.force_table("value")
-        tp.force_contraction("valu")
     wl = Workload(shape, args.warm)
     ms_per_step, wall = wl.timed(args.steps, args.warmup)
     # The timed region holds only the layer's launches, so its event-measured
@@ -354,8 +349,6 @@ def main():
         },
         "wall_s": round(wall, 4),
     }
-    if args.contraction != "mfma":
-        rec["contraction"] = args.contraction
     prof = profile_figures(shape.name, sha)
     if prof:
         rec["roofline"].update(prof)

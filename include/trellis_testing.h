@@ -21,14 +21,6 @@ extern "C" {
  * affected. */
 int trellis_test_force_table(int kind);
 
-/* Contraction of later calls, process-wide: 0 the bf16 MFMA kernels (the
- * default), 1 a VALU variant (v_dot2c_f32_bf16 dot products per lane, x read
- * from LDS per row) where one exists: k = 4, value table, one matrix, m = 5
- * or m = 1; other calls keep MFMA. The variant exists to measure the two
- * against each other and assumes row scales within [2^-110, 2^110] in
- * magnitude. Returns the previous setting, or -2 for a value outside [0, 1]. */
-int trellis_test_force_contraction(int kind);
-
 #ifdef __cplusplus
 }
 #endif

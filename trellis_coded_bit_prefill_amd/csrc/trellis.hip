@@ -504,71 +504,6 @@ __device__ __forceinline__ void unit4_phased(const LaneWords<4> &L, const unsign
   }
 }
 
-// ---- VALU dot contraction (measurement variant) -----------------------------
-// The same k = 4 decode as unit4_phased, but each lane accumulates the dot
-// products of its eight decoded weights with the same eight columns of every
-// x row in VALU registers (v_dot2c_f32_bf16, D rows of x), instead of one bf16
-// MFMA per group. Kept only to measure the two contractions against each
-// other.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-template <int D>
-__device__ __forceinline__ void dot_group(const unsigned char *xrow0, int x_stride, int u, bf16x8 w, float (&dacc)[D]) {
-#pragma unroll
-  for (int m = 0; m < D; ++m) {
-    const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xrow0 + m * x_stride + 16 * u);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const bf16x2 a = {w[2 * p], w[2 * p + 1]};
-      const bf16x2 b = {xv[2 * p], xv[2 * p + 1]};
-      dacc[m] = __builtin_amdgcn_fdot2_f32_bf16(a, b, dacc[m], false);
-    }
-    // one x row in flight at a time: the k = 4 kernel has no registers to
-    // spare for D rows at once
-    if (m + 2 < D) __builtin_amdgcn_sched_barrier(0);
-  }
-}
-template <int TAB, int D>
-__device__ __forceinline__ void unit4_dot(const LaneWords<4> &L, const unsigned char *table, const unsigned char *xrow0,
-                                          int x_stride, float s, float q, float k, uint32_t mask, float (&dacc)[D]) {
-  uint32_t r[2][8];
-  {
-    span4_issue<TAB, 0>(L, table, mask, r);
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 w2 = alu4_weights<2>(L, q, k);
-    const bf16x8 w6 = alu4_weights<6>(L, q, k);
-    __builtin_amdgcn_sched_barrier(0);
-    dot_group<D>(xrow0, x_stride, 2, w2, dacc);
-    dot_group<D>(xrow0, x_stride, 6, w6, dacc);
-    dot_group<D>(xrow0, x_stride, 0, span4_weights<TAB>(r[0], s, q), dacc);
-    dot_group<D>(xrow0, x_stride, 1, span4_weights<TAB>(r[1], s, q), dacc);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    span4_issue<TAB, 4>(L, table, mask, r);
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 w3 = alu4_weights<3>(L, q, k);
-    const bf16x8 w7 = alu4_weights<7>(L, q, k);
-    __builtin_amdgcn_sched_barrier(0);
-    dot_group<D>(xrow0, x_stride, 3, w3, dacc);
-    dot_group<D>(xrow0, x_stride, 7, w7, dacc);
-    dot_group<D>(xrow0, x_stride, 4, span4_weights<TAB>(r[0], s, q), dacc);
-    dot_group<D>(xrow0, x_stride, 5, span4_weights<TAB>(r[1], s, q), dacc);
-  }
-}
-// Adds the lanes' dot partials to an MFMA-layout tile (lane (j, g) holds rows
-// 4g .. 4g+3 of column j): the four k-groups of column j are summed across
-// lanes j, j+16, j+32, j+48 first. Clears the partials.
-template <int D>
-__device__ __forceinline__ void fold_dot(float (&dacc)[D], f32x4 &acc, int g) {
-#pragma unroll
-  for (int m = 0; m < D; ++m) {
-    float t = dacc[m] + __shfl_xor(dacc[m], 16);
-    t += __shfl_xor(t, 32);
-    if (m / 4 == g) acc[m % 4] += t;
-    dacc[m] = 0.f;
-  }
-}
-
 template <int BITS, int MASK, int TAB, bool EXACT, int... U>
 __device__ __forceinline__ void unit(const LaneWords<BITS> &L, const unsigned char *table, const unsigned char *xa,
                                      float s, float q, float k, uint32_t mask, f32x4 &acc,
@@ -693,7 +628,7 @@ __device__ __forceinline__ void sum_partials(const Plan &pl, float *ws, int tile
 // of both matrices, decoded in two steps (gate, then up) against the same x
 // into two accumulators, so whichever wave completes a tile holds both sums
 // and writes the elementwise tail directly.
-template <int BITS, int MASK, int TAB, bool TWO, int DOTM = 0>
+template <int BITS, int MASK, int TAB, bool TWO>
 __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__restrict__ codes,
                                                              const uint16_t *__restrict__ scales,
                                                              const uint32_t *__restrict__ codes2,
@@ -927,7 +862,6 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     alu_row_constants(s, q, kq);
     bool out_of_range = !__all(alu_scale_ok(s));
     f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};  // second matrix (up)
-    float dacc[DOTM > 0 ? DOTM : 1] = {};  // VALU-dot partials (measurement variant)
     // table byte-address mask (SDWA operand)
     const uint32_t mask_addr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
     int u = u0;
@@ -941,7 +875,6 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       f32x4 &A = kUp ? acc2 : acc;
       if constexpr (!kUp) {
         if (tile != cur) {
-          if constexpr (DOTM > 0) fold_dot<DOTM>(dacc, acc, g);
           tile_done(cur, acc, acc2);
           cur = tile;
           acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -969,11 +902,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(C.w, table, xb, ss, qq, kk, mask_addr, A,
                                                           std::make_integer_sequence<int, 8>{});
       else if constexpr (BITS == 4 && MASK == 0x33 && TAB != kPairTable)
-        if constexpr (DOTM > 0)
-          unit4_dot<TAB, DOTM>(C.w, table, xl + (192 - 64 * g) * 2 + b * 512, pl.x_stride, ss, qq, kk, mask_addr,
-                               dacc);
-        else
-          unit4_phased<TAB>(C.w, table, xb, ss, qq, kk, mask_addr, A);
+        unit4_phased<TAB>(C.w, table, xb, ss, qq, kk, mask_addr, A);
       else
         unit<BITS, MASK, TAB, false>(C.w, table, xb, ss, qq, kk, mask_addr, A, std::make_integer_sequence<int, 8>{});
       if constexpr (TWO && !kUp) return;  // the unit's up block follows
@@ -1004,7 +933,6 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       }
       step(S1, S0, std::false_type{}, UpInSlot1{});
     }
-    if constexpr (DOTM > 0) fold_dot<DOTM>(dacc, acc, g);
     tl = cur;
     if (cross(cur)) stage(cur, acc, acc2);
     else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp)
@@ -1216,15 +1144,11 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
 // Prefill kernels: k = 2, 3, 4 with the value or the code table, and k = 2
 // with the pair table, each for one matrix or for gate and up. Variant =
 // 2 * (k - 2) + table kind, pair = 6; plus kTables for two matrices.
-// Two more: the VALU-dot measurement variants (k = 4, value table, one
-// matrix) for M = 5 and M = 1.
-enum Variant { kVariantPair = 6, kTables = 7, kVariantDot5 = 2 * kTables, kVariantDot1, kVariants };
+enum Variant { kVariantPair = 6, kTables = 7, kVariants = 2 * kTables };
 constexpr int variant_of(int bits, int tab, bool two) {
   return (tab == kPairTable ? kVariantPair : 2 * (bits - 2) + tab) + (two ? kTables : 0);
 }
-constexpr int variant_table(int v) {
-  return v >= kVariantDot5 ? kValueTable : v % kTables == kVariantPair ? kPairTable : v % kTables % 2;
-}
+constexpr int variant_table(int v) { return v % kTables == kVariantPair ? kPairTable : v % kTables % 2; }
 
 struct DeviceState {
   int cus = 0;
@@ -1273,11 +1197,7 @@ PrefillFn prefill_fn_of(int v) {
     default: return &prefill_kernel<2, Mix<2, true>::kMask, kPairTable, TWO>;
   }
 }
-PrefillFn prefill_fn(int v) {
-  if (v == kVariantDot5) return &prefill_kernel<4, Mix<4>::kMask, kValueTable, false, 5>;
-  if (v == kVariantDot1) return &prefill_kernel<4, Mix<4>::kMask, kValueTable, false, 1>;
-  return v >= kTables ? prefill_fn_of<true>(v - kTables) : prefill_fn_of<false>(v);
-}
+PrefillFn prefill_fn(int v) { return v >= kTables ? prefill_fn_of<true>(v - kTables) : prefill_fn_of<false>(v); }
 
 trellis_status device_state(DeviceState *&st, int v) {
   int dev = 0;
@@ -1378,11 +1298,6 @@ namespace {
 // to k = 2 only). One relaxed atomic load per call, no environment lookup.
 std::atomic<int> g_force_table{-1};
 
-// Contraction override for measurement (trellis_test_force_contraction): 1
-// runs the VALU-dot variant where it exists (k = 4, value table, one matrix,
-// M = 5 or 1), 0 the MFMA kernels.
-std::atomic<int> g_force_dot{0};
-
 int table_override(int bits) {
   const int t = g_force_table.load(std::memory_order_relaxed);
   if (t == kPairTable && bits != 2) return -1;
@@ -1430,10 +1345,7 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
       }
     }
   }
-  int v = variant_of(g.bits, tab, two);
-  if (g_force_dot.load(std::memory_order_relaxed) == 1 && g.bits == 4 && tab == kValueTable && !two &&
-      (m == 5 || m == 1))
-    v = m == 5 ? kVariantDot5 : kVariantDot1;
+  const int v = variant_of(g.bits, tab, two);
   DeviceState *st = nullptr;
   trellis_status rc = device_state(st, v);
   if (rc != TRELLIS_OK) return rc;
@@ -1588,11 +1500,6 @@ trellis_status trellis_prefill_noalloc(const uint16_t *x_bf16, int32_t m, const 
     orow[i] = out_bf16 + (size_t)i * g.n;
   }
   return launch_rows(xr, orow, m, codes, scales_bf16, nullptr, nullptr, g, stream, true);
-}
-
-int trellis_test_force_contraction(int kind) {
-  if (kind < 0 || kind > 1) return -2;
-  return g_force_dot.exchange(kind);
 }
 
 int trellis_test_force_table(int kind) {
