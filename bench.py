@@ -273,8 +273,6 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' figures")
     ap.add_argument("--extra-steps", type=int, default=300,
                     help="timed steps per extra workload (after as many warm-up steps)")
-    ap.add_argument("--prefill-kernel", type=int, choices=(0, 1, 2), default=0,
-                    help="tuning: 0 the library's choice, 1 LDS-staged x, 2 x in registers")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -305,8 +303,6 @@ def main():
     torch.cuda.set_device(dev)
     tp.load_library()
 
-    if args.prefill_kernel:
-        tp.force_kernel(args.prefill_kernel)
     wl = Workload(shape, args.warm)
     ms_per_step, wall = wl.timed(args.steps, args.warmup)
     # The timed region holds only the layer's launches, so its event-measured

@@ -21,12 +21,6 @@ extern "C" {
  * affected. */
 int trellis_test_force_table(int kind);
 
-/* Prefill kernel of later calls, process-wide: 0 the library's choice (the
- * default), 1 the LDS-staged-x kernel, 2 the kernel that keeps x in registers
- * and its tiles block-major (not used by trellis_prefill_noalloc). Returns
- * the previous setting, or -2 for a value outside [0, 2]. */
-int trellis_test_force_kernel(int kind);
-
 #ifdef __cplusplus
 }
 #endif

@@ -29,12 +29,3 @@ def force_table():
     yield tp.force_table
     tp.force_table(None)
 
-
-def pytest_sessionstart(session):
-    # TRELLIS_TEST_KERNEL=1|2 runs the whole suite on one prefill kernel
-    # (test hook trellis_test_force_kernel); unset: the library's choice.
-    kind = os.environ.get("TRELLIS_TEST_KERNEL")
-    if kind:
-        import trellis_coded_bit_prefill_amd as tp
-
-        tp.force_kernel(int(kind))

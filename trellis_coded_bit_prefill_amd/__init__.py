@@ -40,7 +40,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTED = ("trellis_supported", "trellis_decode", "trellis_prefill", "trellis_matvec", "trellis_prefill_packed",
             "trellis_gate_up", "trellis_prefill_noalloc", "trellis_status_string")
 # Test and tuning hooks (include/trellis_testing.h).
-EXPORTED_TESTING = ("trellis_test_force_table", "trellis_test_force_kernel")
+EXPORTED_TESTING = ("trellis_test_force_table",)
 TABLES = {"value": 0, "code": 1, "pair": 2}
 
 
@@ -104,8 +104,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.trellis_gate_up.restype = ctypes.c_int
     L.trellis_prefill_noalloc.argtypes = [vp, ctypes.c_int32, vp, vp, Geom, vp, vp]
     L.trellis_prefill_noalloc.restype = ctypes.c_int
-    L.trellis_test_force_kernel.argtypes = [ctypes.c_int]
-    L.trellis_test_force_kernel.restype = ctypes.c_int
     L.trellis_test_force_table.argtypes = [ctypes.c_int]
     L.trellis_test_force_table.restype = ctypes.c_int
     _lib = L
@@ -121,15 +119,6 @@ def force_table(name):
     if prev < -1:
         raise ValueError(f"bad table {name!r}")
     return None if prev == -1 else {v: k for k, v in TABLES.items()}[prev]
-
-
-def force_kernel(kind: int) -> int:
-    """Test hook: 0 the library's choice of prefill kernel, 1 the LDS-staged-x
-    kernel, 2 the x-in-registers kernel. Returns the previous setting."""
-    prev = load_library().trellis_test_force_kernel(kind)
-    if prev < 0:
-        raise ValueError(f"bad kernel {kind!r}")
-    return prev
 
 
 def status_string(status: int) -> str:

@@ -1068,609 +1068,6 @@ template <> struct Mix<2, true> { static constexpr int kMask = 0b11111111; };
 template <> struct Mix<3> { static constexpr int kMask = 0b01010101; };
 template <> struct Mix<4> { static constexpr int kMask = 0b00110011; };
 
-// ===========================================================================
-// prefill2_kernel: x in registers, block-major tiles inside each workgroup
-// ===========================================================================
-// The same layer with no x staging in LDS, so LDS holds only the decode table
-// (which lets k = 2 and k = 3 use tables of window pairs, 64 and 128 KB).
-//   * Units (16-row tile x 256-weight block) in tile-major order are split
-//     evenly over the workgroups (stream-K, as above); a workgroup's range
-//     holds at most two tiles it shares with other workgroups ("cross": its
-//     first and last tile when the range starts or ends inside them) and any
-//     number of tiles it owns whole.
-//   * Inside the workgroup the owned tiles go in rounds of at most kOwnMax;
-//     a round's units are ordered block-major (every owned tile of the round
-//     at block 0, then at block 1, ...), the cross units come first in round
-//     0, and each round's list is split into kW2 contiguous pieces, one per
-//     wave. A wave keeps one accumulator per tile slot (two cross, kOwnMax
-//     owned), so one x block, loaded into registers straight from memory,
-//     serves every tile of the round at that block.
-//   * At the end of a round the waves' accumulators are summed through LDS in
-//     wave order and the owned tiles stored; the cross tiles' sums (after the
-//     last round) go through the workspace as one partial per workgroup, the
-//     last workgroup to arrive (per-tile counter) adding them in workgroup
-//     order.
-constexpr int kW2 = 16;                // waves per workgroup: four per SIMD, 128 VGPRs each
-constexpr int kThreads2 = kW2 * kWave;
-constexpr int kOwnMax = 6;             // owned tiles per round (at most; the plan sets it)
-constexpr int kCodeTemp = 4096 * 2;    // float16 code table, the source of the pair tables
-enum { kPair3Table = 3 };              // k = 3: 15-bit pair of windows -> two float16 codes
-constexpr int table2_bytes(int tab) {
-  return tab == kPair3Table ? 32768 * 4 : tab == kPairTable ? 16384 * 4 : tab == kCodeTable ? 4096 * 2 : 4096 * 4;
-}
-
-struct Plan2 {
-  int32_t m, n, k;
-  int32_t kb;         // 256-weight blocks per row
-  int32_t tiles;      // ceil(N / 16)
-  int32_t groups;     // workgroups
-  int32_t cq, cr;     // units per workgroup: cq, plus one for the first cr
-  int32_t maxc;       // workspace slots per tile (workgroups sharing one tile)
-  int32_t own;        // owned tiles per round
-  int32_t slot_lanes; // lanes holding output rows below M: 16 * ceil(M / 4)
-  int32_t slots_off;  // LDS byte offset of the per-wave sum slots
-  int32_t lds_bytes;
-};
-
-__device__ __forceinline__ int wg_of2(int u, const Plan2 &pl) {
-  const int cut = pl.cr * (pl.cq + 1);
-  return u < cut ? (int)((uint32_t)u / (uint32_t)(pl.cq + 1)) : pl.cr + (int)((uint32_t)(u - cut) / (uint32_t)pl.cq);
-}
-
-// ---- k = 3 pair table --------------------------------------------------------
-// For k = 3 the windows of weights idx and idx + 1 (idx even) overlap in 9
-// bits: the 15 stream bits from the lower window's start hold both. Entry p of
-// the 32768-entry table holds code(p >> 3) (weight idx) in its high float16
-// half and code(p & 0xFFF) (weight idx + 1) in its low half.
-template <int P, int N>
-__device__ __forceinline__ uint32_t pair3_xa(const uint32_t (&D)[N]) {
-  // byte address p * 4: stream bits [P - 2, P + 15) masked to bits [2, 17)
-  constexpr int sh = P - 2;
-  if constexpr (sh < 0) {
-    static_assert(sh == -2, "unexpected pair offset");
-    return (D[0] << 2) & 0x1FFFCu;
-  } else {
-    constexpr int w = sh >> 5, r = sh & 31;
-    if constexpr (r + 17 <= 32) {
-      return (D[w] >> r) & 0x1FFFCu;
-    } else {
-      static_assert(w + 1 < N, "pair outside the lane's words");
-      return __builtin_amdgcn_alignbit(D[w + 1], D[w], r) & 0x1FFFCu;
-    }
-  }
-}
-template <int U, int... I>
-__device__ __forceinline__ bf16x8 group_pair3(const uint32_t (&D)[7], const unsigned char *table, float q,
-                                              std::integer_sequence<int, I...>) {
-  // pair i of group U: weights idx = 8U + 2i, idx + 1; the lower window at
-  // local bit (62 - idx) * 3
-  const uint32_t e[4] = {*reinterpret_cast<const uint32_t *>(table + pair3_xa<(62 - 8 * U - 2 * I) * 3>(D))...};
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = mix_hi(e[i], q);
-    f[2 * i + 1] = mix_lo(e[i], q);
-  }
-  bf16x8 w;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
-  return w;
-}
-
-// ---- decode of one unit into eight B operands ------------------------------
-template <int BITS, int MASK, int TAB, int U>
-__device__ __forceinline__ void dec_group(const LaneWords<BITS> &L, const unsigned char *table, float s, float q,
-                                          float k, uint32_t mask, bf16x8 (&w)[8]) {
-  if constexpr (TAB == kPairTable) {
-    static_assert(BITS == 2, "the pair table is for k = 2");
-    constexpr bool span = ((MASK >> (U - U % 2)) & 3) == 3;
-    if constexpr (span && U % 2 == 0) {
-      bf16x8 t[2];
-      pair_span<U>(L.d, table, q, mask, t);
-      w[U] = t[0];
-      w[U + 1] = t[1];
-    } else if constexpr (!span) {
-      static_assert(((MASK >> U) & 1) == 0, "pair-table groups come in aligned pairs");
-      w[U] = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
-    }
-  } else if constexpr (TAB == kPair3Table) {
-    static_assert(BITS == 3, "the 15-bit pair table is for k = 3");
-    if constexpr ((MASK >> U) & 1)
-      w[U] = group_pair3<U>(L.d, table, q, std::make_integer_sequence<int, 4>{});
-    else
-      w[U] = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
-  } else if constexpr (span_start<BITS, MASK, U>()) {
-    table_span<BITS, TAB, U>(L, table, s, q, mask, &w[U]);
-  } else if constexpr (!in_span<BITS, MASK, U>()) {
-    if constexpr ((MASK >> U) & 1)
-      w[U] = group_table<BITS, TAB, U>(L, table, s, q, std::make_integer_sequence<int, 8>{});
-    else
-      w[U] = group_alu<BITS, U>(L, q, k, std::make_integer_sequence<int, 8>{});
-  }
-}
-
-// A unit is decoded and contracted in two halves of four groups, so only
-// four B operands are live at a time. Half H of group set G: the groups whose
-// index appears in Half<...>::g.
-template <int BITS, int MASK, int TAB> struct Halves {
-  static constexpr int g[2][4] = {{0, 1, 2, 3}, {4, 5, 6, 7}};
-};
-// k = 4 with the 4 + 4 mix: each half holds one table span (two groups) and
-// two ALU groups, so the span's gathers are in flight during the ALU work.
-template <int TAB> struct Halves<4, 0x33, TAB> {
-  static constexpr int g[2][4] = {{0, 1, 2, 6}, {4, 5, 3, 7}};
-};
-
-// Pair-table halves with every gather issued before the first one is used
-// (groups 4H .. 4H+3, four pair entries per group, 16 per half).
-template <int H, int... I>
-__device__ __forceinline__ void half_pair3(const uint32_t (&D)[7], const unsigned char *table, float q, bf16x8 (&w)[4],
-                                           std::integer_sequence<int, I...>) {
-  // entry I: group 4H + I / 4, pair I % 4 (weights idx = 8U + 2(I % 4), idx + 1)
-  const uint32_t a[16] = {pair3_xa<(62 - 8 * (4 * H + I / 4) - 2 * (I % 4)) * 3>(D)...};
-  const uint32_t e[16] = {*reinterpret_cast<const uint32_t *>(table + a[I])...};
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int gi = 0; gi < 4; ++gi) {
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = mix_hi(e[4 * gi + i], q);
-      f[2 * i + 1] = mix_lo(e[4 * gi + i], q);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[gi][i] = (__bf16)f[i];
-  }
-}
-template <int H, int N>
-__device__ __forceinline__ void half_pair2(const uint32_t (&D)[N], const unsigned char *table, float q, uint32_t mask,
-                                           bf16x8 (&w)[4]) {
-  // spans (4H, 4H+1) and (4H+2, 4H+3); pair field i of span U holds pair i
-  // of group U + 1 (low half of the shifted word) and of group U (high half)
-  uint32_t a[2][4][2];
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      constexpr int U0 = 4 * H;
-      switch (sp * 4 + i) {
-        case 0: pair_x4<108 - 16 * U0 - 0>(D, mask, a[0][0]); break;
-        case 1: pair_x4<108 - 16 * U0 - 4>(D, mask, a[0][1]); break;
-        case 2: pair_x4<108 - 16 * U0 - 8>(D, mask, a[0][2]); break;
-        case 3: pair_x4<108 - 16 * U0 - 12>(D, mask, a[0][3]); break;
-        case 4: pair_x4<108 - 16 * (U0 + 2) - 0>(D, mask, a[1][0]); break;
-        case 5: pair_x4<108 - 16 * (U0 + 2) - 4>(D, mask, a[1][1]); break;
-        case 6: pair_x4<108 - 16 * (U0 + 2) - 8>(D, mask, a[1][2]); break;
-        default: pair_x4<108 - 16 * (U0 + 2) - 12>(D, mask, a[1][3]); break;
-      }
-    }
-  }
-  uint32_t e[2][4][2];
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) e[sp][i][h] = *reinterpret_cast<const uint32_t *>(table + a[sp][i][h]);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
-    float f[2][8];  // [group U + 1, group U]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[0][2 * i] = mix_hi(e[sp][i][0], q);
-      f[0][2 * i + 1] = mix_lo(e[sp][i][0], q);
-      f[1][2 * i] = mix_hi(e[sp][i][1], q);
-      f[1][2 * i + 1] = mix_lo(e[sp][i][1], q);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      w[2 * sp][i] = (__bf16)f[1][i];      // group 4H + 2sp
-      w[2 * sp + 1][i] = (__bf16)f[0][i];  // group 4H + 2sp + 1
-    }
-  }
-}
-
-template <int BITS, int MASK, int TAB, int H>
-__device__ __forceinline__ void decode_half(const LaneWords<BITS> &L, const unsigned char *table, float s, float q,
-                                            float k, uint32_t mask, bf16x8 (&w)[4]) {
-  constexpr auto &G = Halves<BITS, MASK, TAB>::g[H];
-  if constexpr (BITS == 4 && MASK == 0x33 && (TAB == kValueTable || TAB == kCodeTable)) {
-    uint32_t r[2][8];
-    span4_issue<TAB, 4 * H>(L, table, mask, r);
-    __builtin_amdgcn_sched_barrier(0);
-    w[2] = alu4_weights<G[2]>(L, q, k);
-    w[3] = alu4_weights<G[3]>(L, q, k);
-    __builtin_amdgcn_sched_barrier(0);
-    w[0] = span4_weights<TAB>(r[0], s, q);
-    w[1] = span4_weights<TAB>(r[1], s, q);
-  } else if constexpr (TAB == kPair3Table && MASK == 0xFF) {
-    half_pair3<H>(L.d, table, q, w, std::make_integer_sequence<int, 16>{});
-  } else if constexpr (TAB == kPairTable && MASK == 0xFF) {
-    half_pair2<H>(L.d, table, q, mask, w);
-  } else {
-    bf16x8 all[8];
-    dec_group<BITS, MASK, TAB, G[0]>(L, table, s, q, k, mask, all);
-    dec_group<BITS, MASK, TAB, G[1]>(L, table, s, q, k, mask, all);
-    dec_group<BITS, MASK, TAB, G[2]>(L, table, s, q, k, mask, all);
-    dec_group<BITS, MASK, TAB, G[3]>(L, table, s, q, k, mask, all);
-    w[0] = all[G[0]];
-    w[1] = all[G[1]];
-    w[2] = all[G[2]];
-    w[3] = all[G[3]];
-  }
-}
-// Rows whose scale is outside the ALU path's exact range: the pages' chain on
-// the ALU for every group.
-template <int BITS, int MASK, int TAB, int H>
-__device__ __forceinline__ void decode_half_exact(const LaneWords<BITS> &L, float s, bf16x8 (&w)[4]) {
-  constexpr auto &G = Halves<BITS, MASK, TAB>::g[H];
-  w[0] = group_exact<BITS, G[0]>(L, s, std::make_integer_sequence<int, 8>{});
-  w[1] = group_exact<BITS, G[1]>(L, s, std::make_integer_sequence<int, 8>{});
-  w[2] = group_exact<BITS, G[2]>(L, s, std::make_integer_sequence<int, 8>{});
-  w[3] = group_exact<BITS, G[3]>(L, s, std::make_integer_sequence<int, 8>{});
-}
-
-template <int BITS, int MASK, int TAB, int H>
-__device__ __forceinline__ void mfma4(const bf16x8 (&x)[8], const bf16x8 (&w)[4], f32x4 &acc) {
-  constexpr auto &G = Halves<BITS, MASK, TAB>::g[H];
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[G[0]], w[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[G[1]], w[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[G[2]], w[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[G[3]], w[3], acc, 0, 0, 0);
-}
-// Position of a unit in a workgroup's round list.
-struct Pos2 {
-  int t, b, slot;
-};
-
-// Partials of cross tiles: slot [tile][workgroup index among the tile's
-// contributors] holds NH 16x16 fp32 partials, lane-major, 1 KB each.
-template <int NH>
-__device__ __forceinline__ float *partial_slot2(const Plan2 &pl, float *ws, int tile, int idx) {
-  return ws + ((size_t)tile * pl.maxc + idx) * NH * 256;
-}
-
-// Output row pointer r of the call (r < 16), read from the kernel arguments.
-__device__ __forceinline__ uint16_t *out_row(const RowPtrs &rp, int r) {
-  uint16_t *p = rp.out[0];
-#pragma unroll
-  for (int i = 1; i < kMaxRows; ++i)
-    if (r == i) p = rp.out[i];
-  return p;
-}
-// store_tile with the row pointers taken from the kernel arguments.
-__device__ __forceinline__ void store_tile2(const RowPtrs &rp, f32x4 v, int m, int ncols, int col, int g) {
-  if (col >= ncols) return;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (4 * g + e < m) out_row(rp, 4 * g + e)[col] = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-}
-
-template <int BITS, int MASK, int TAB>
-__global__ __launch_bounds__(kThreads2) void prefill2_kernel(const uint32_t *__restrict__ codes,
-                                                             const uint16_t *__restrict__ scales,
-                                                             const uint32_t *__restrict__ codes2,
-                                                             const uint16_t *__restrict__ scales2,
-                                                             float *__restrict__ ws, uint32_t *__restrict__ counters,
-                                                             Plan2 pl, RowPtrs rp) {
-  constexpr int NH = 1;
-  const int OWN = pl.own;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char *const table = lds;
-  constexpr int wpb = 8 * BITS;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int j = lane & 15, g = lane >> 4;
-  const int c = blockIdx.x;
-  const int kb = pl.kb;
-
-  // ---- this workgroup's units and tiles (wave-uniform) ----
-  const int U0 = c * pl.cq + (c < pl.cr ? c : pl.cr);
-  const int U1 = U0 + pl.cq + (c < pl.cr ? 1 : 0);
-  const int tf = (int)((uint32_t)U0 / (uint32_t)kb), bfirst = U0 - tf * kb;
-  const int tl = (int)((uint32_t)(U1 - 1) / (uint32_t)kb), bend = U1 - tl * kb;
-  bool x0 = false, x1 = false;  // cross first / cross last
-  int n0 = 0, n1 = 0, own_lo = tf, n_own = 0;
-  if (tf == tl) {
-    if (bfirst == 0 && bend == kb) {
-      n_own = 1;
-    } else {
-      x0 = true;
-      n0 = bend - bfirst;
-    }
-  } else {
-    x0 = bfirst != 0;
-    x1 = bend != kb;
-    n0 = x0 ? kb - bfirst : 0;
-    n1 = x1 ? bend : 0;
-    own_lo = x0 ? tf + 1 : tf;
-    n_own = (x1 ? tl - 1 : tl) - own_lo + 1;
-  }
-  const int rounds = n_own > 0 ? (n_own + OWN - 1) / OWN : 1;
-
-  // ---- prologue: decode table ----
-  if constexpr (TAB == kPairTable || TAB == kPair3Table) {
-    // float16 codes of all windows first (in the region after the table),
-    // then the pair entries from them: entry p = code(p >> S) : code(p & 0xFFF)
-    uint16_t *ct = reinterpret_cast<uint16_t *>(lds + table2_bytes(TAB));
-    for (int e = tid; e < 2048; e += kThreads2)
-      reinterpret_cast<uint32_t *>(ct)[e] = code_entry_pair((uint32_t)e);
-    __syncthreads();
-    constexpr int S = TAB == kPair3Table ? 3 : 2;   // entries per high window: 2^S
-    for (int h = tid; h < 4096; h += kThreads2) {
-      const uint32_t hi = (uint32_t)ct[h] << 16;
-      const int lo0 = (h << S) & 0xFFF;
-      uint32_t e[1 << S];
-#pragma unroll
-      for (int i = 0; i < (1 << S); ++i) e[i] = hi | ct[lo0 + i];
-      uint4 *dst = reinterpret_cast<uint4 *>(table + (size_t)h * (4 << S));
-#pragma unroll
-      for (int i = 0; i < (1 << S) / 4; ++i) dst[i] = uint4{e[4 * i], e[4 * i + 1], e[4 * i + 2], e[4 * i + 3]};
-    }
-  } else if constexpr (TAB == kCodeTable) {
-    for (int e = tid; e < 2048; e += kThreads2) reinterpret_cast<uint32_t *>(table)[e] = code_entry_pair((uint32_t)e);
-  } else {
-    for (int e = tid; e < 4096; e += kThreads2)
-      reinterpret_cast<uint32_t *>(table)[e] = __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)e)));
-  }
-  __syncthreads();
-
-  // ---- per-lane addressing ----
-  const uint32_t row_bytes = (uint32_t)kb * wpb * 4;
-  const uint32_t lane_off = (uint32_t)j * row_bytes + (uint32_t)g * (8 * BITS);
-  const uint32_t lane_off_next = (uint32_t)j * row_bytes + (uint32_t)((2 * BITS * (g + 1)) % wpb) * 4;
-  const uint32_t lane_off_scale = (uint32_t)j * 2;
-  const int xrow = j < pl.m ? j : pl.m - 1;
-  const uint16_t *xr0 = rp.x[0];
-#pragma unroll
-  for (int r = 1; r < kMaxRows; ++r)
-    if (xrow == r) xr0 = rp.x[r];
-  const uint16_t *const xr = xr0 + (192 - 64 * g);
-  auto unit_buffer = [&](int t, int bb, bool second) {
-    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
-    const uint32_t blk_off = (uint32_t)bb * (wpb * 4);
-    const unsigned char *base = reinterpret_cast<const unsigned char *>(second ? codes2 : codes) +
-                                (int64_t)t * 16 * row_bytes + blk_off;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(base), (short)0,
-                                             (int)((uint32_t)rows * row_bytes - blk_off), kRawBufferWord3);
-  };
-  auto scale_buffer = [&](int t, bool second) {
-    const int rows = pl.n - t * 16 < 16 ? pl.n - t * 16 : 16;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((second ? scales2 : scales) + (int64_t)t * 16),
-                                             (short)0, rows * 2, kRawBufferWord3);
-  };
-  struct Slot {
-    LaneWords<BITS> w[NH];
-    uint32_t scb[NH];
-  };
-  auto request = [&](Slot &S, const Pos2 &p) {
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      load_words<BITS>(unit_buffer(p.t, p.b, h == 1), lane_off, lane_off_next, S.w[h]);
-      S.scb[h] = __builtin_amdgcn_raw_buffer_load_b16(scale_buffer(p.t, h == 1), lane_off_scale, 0, 0);
-    }
-  };
-  auto load_x = [&](bf16x8 (&xv)[8], int bb) {
-    const bf16x8 *src = reinterpret_cast<const bf16x8 *>(xr + (int64_t)bb * 256);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) xv[u] = src[u];
-  };
-  // The x operands of one half of the groups (those its MFMAs read).
-  auto load_x_half = [&](bf16x8 (&xv)[8], int bb, auto half) {
-    constexpr auto &G = Halves<BITS, MASK, TAB>::g[decltype(half)::value];
-    const bf16x8 *src = reinterpret_cast<const bf16x8 *>(xr + (int64_t)bb * 256);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xv[G[i]] = src[G[i]];
-  };
-  const uint32_t mask_addr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
-
-  // Per-wave running sums of every tile slot, [slot][matrix][wave][lane]; the
-  // combine at the end of a round reads them directly.
-  // Only lanes holding output rows below M (lanes < slot_lanes) keep sums.
-  f32x4 *const slots = reinterpret_cast<f32x4 *>(lds + pl.slots_off);
-  const bool keeps = lane < pl.slot_lanes;
-  auto slot_at = [&](int s, int h, int w) -> f32x4 & {
-    return slots[((s * NH + h) * kW2 + w) * pl.slot_lanes + lane];
-  };
-  if (keeps)
-    for (int s = 0; s < OWN + 2; ++s) slot_at(s, 0, wave) = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int round = 0; round < rounds; ++round) {
-    const int t_own0 = own_lo + round * OWN;
-    const int R = n_own > 0 ? min(OWN, n_own - round * OWN) : 0;
-    const int ncr = round == 0 ? n0 + n1 : 0;
-    const int L = ncr + R * kb;
-    const int base = L / kW2, rem = L - base * kW2;
-    const int i0 = wave * base + (wave < rem ? wave : rem);
-    const int i1 = i0 + base + (wave < rem ? 1 : 0);
-    // position of list index i
-    auto pos_of = [&](int i) {
-      Pos2 p;
-      if (i < n0 && ncr) {
-        p.t = tf; p.b = bfirst + i; p.slot = 0;
-      } else if (i < ncr) {
-        p.t = tl; p.b = i - n0; p.slot = 1;
-      } else {
-        const int jj = i - ncr;
-        p.b = (int)((uint32_t)jj / (uint32_t)R);
-        const int r = jj - p.b * R;
-        p.t = t_own0 + r;
-        p.slot = 2 + r;
-      }
-      return p;
-    };
-    auto advance = [&](Pos2 &p, int i_next) {
-      if (i_next < ncr || i_next == ncr) {
-        p = pos_of(i_next);
-      } else if (p.slot + 1 < 2 + R) {
-        ++p.t; ++p.slot;
-      } else {
-        p.t = t_own0; p.slot = 2; ++p.b;
-      }
-    };
-    if (i0 < i1) {
-      // Code words of unit i live in slot i % 2 and are requested one unit
-      // ahead; past the piece's end the last unit is requested again,
-      // so every step issues the same loads and the compiler's memory-counter
-      // waits stay exact. x of a block is requested when the block starts,
-      // before the next unit's code words, so waiting for it does not wait
-      // for them; the first half's decode covers its latency.
-      // The tile's running sum lives in this wave's LDS slot: read when the
-      // tile changes, written back when it changes again (consecutive units
-      // of one tile keep it in registers).
-      Slot S0, S1;
-      bf16x8 xc[8];
-      Pos2 cur = pos_of(i0);
-      Pos2 rq = cur;
-      int ri = i0;
-      auto advance_req = [&]() {
-        if (ri + 1 < i1) {
-          ++ri;
-          advance(rq, ri);
-        }
-      };
-      request(S0, rq);
-      int aslot = -1;  // slot whose sum is in `a`
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-      load_x(xc, cur.b);
-      int i = i0;
-      auto step = [&](Slot &C, Slot &N) {
-        const bool has_next = i + 1 < i1;
-        Pos2 nxt = cur;
-        if (has_next) advance(nxt, i + 1);
-        // x of the next unit's block replaces each half's x operands once
-        // that half's MFMAs have read them
-        const bool new_block = has_next && nxt.b != cur.b;
-        advance_req();
-        request(N, rq);
-        if (cur.slot != aslot) {
-          if (keeps) {
-            if (aslot >= 0) slot_at(aslot, 0, wave) = a;
-            a = slot_at(cur.slot, 0, wave);
-          }
-          aslot = cur.slot;
-        }
-        const float s = bf16_bits_to_f32((uint16_t)C.scb[0]);
-        float q, kq;
-        alu_row_constants(s, q, kq);
-        if (__builtin_expect(!__all(alu_scale_ok(s)), 0)) {
-          {
-            bf16x8 w[4];
-            decode_half_exact<BITS, MASK, TAB, 0>(C.w[0], s, w);
-            mfma4<BITS, MASK, TAB, 0>(xc, w, a);
-          }
-          if (new_block) load_x_half(xc, nxt.b, std::integral_constant<int, 0>{});
-          {
-            bf16x8 w[4];
-            decode_half_exact<BITS, MASK, TAB, 1>(C.w[0], s, w);
-            mfma4<BITS, MASK, TAB, 1>(xc, w, a);
-          }
-          if (new_block) load_x_half(xc, nxt.b, std::integral_constant<int, 1>{});
-        } else {
-          {
-            bf16x8 w[4];
-            decode_half<BITS, MASK, TAB, 0>(C.w[0], table, s, q, kq, mask_addr, w);
-            mfma4<BITS, MASK, TAB, 0>(xc, w, a);
-          }
-          if (new_block) load_x_half(xc, nxt.b, std::integral_constant<int, 0>{});
-          {
-            bf16x8 w[4];
-            decode_half<BITS, MASK, TAB, 1>(C.w[0], table, s, q, kq, mask_addr, w);
-            mfma4<BITS, MASK, TAB, 1>(xc, w, a);
-          }
-          if (new_block) load_x_half(xc, nxt.b, std::integral_constant<int, 1>{});
-        }
-        ++i;
-        cur = nxt;
-        const int left = i1 - i;
-        if (left >= 3) __builtin_amdgcn_s_setprio(3);
-        else if (left == 2) __builtin_amdgcn_s_setprio(2);
-        else __builtin_amdgcn_s_setprio(1);
-      };
-      for (;;) {
-        step(S0, S1);
-        if (i == i1) break;
-        step(S1, S0);
-        if (i == i1) break;
-      }
-      if (keeps) slot_at(aslot, 0, wave) = a;
-      __builtin_amdgcn_s_setprio(0);
-    }
-
-    // ---- combine: the waves' sums (in their LDS slots) added in wave order ----
-    const bool final_round = round + 1 == rounds;
-    const int s_lo = final_round ? (x0 ? 0 : x1 ? 1 : 2) : 2;
-    const int s_hi = 2 + R;  // exclusive
-    __syncthreads();
-    for (int s = s_lo + wave; s < s_hi; s += kW2) {
-      if (s < 2 && !(s == 0 ? x0 : x1)) continue;
-      f32x4 sum[NH];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        sum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (keeps)
-          for (int w = 0; w < kW2; ++w) {
-            const f32x4 v = slot_at(s, h, w);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum[h][e] += v[e];
-          }
-      }
-      if (s >= 2) {
-        store_tile2(rp, sum[0], pl.m, pl.n, (t_own0 + s - 2) * 16 + j, g);
-        continue;
-      }
-      // cross tile: this workgroup's partial to the workspace; the last
-      // workgroup to arrive adds all partials in workgroup order and stores.
-      const int T = s == 0 ? tf : tl;
-      const int first = wg_of2(T * kb, pl), lastw = wg_of2(T * kb + kb - 1, pl);
-      const int nc = lastw - first + 1;
-      float *mine = partial_slot2<NH>(pl, ws, T, c - first);
-#pragma unroll
-      for (int h = 0; h < NH; ++h) stage_partial(mine + h * 256 + 4 * lane, sum[h]);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      uint32_t old = 0;
-      if (lane == 0) old = __hip_atomic_fetch_add(&counters[T], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __builtin_amdgcn_readfirstlane(old);
-      if ((int)old + 1 != nc) continue;
-      constexpr int kSc1 = 16;  // cache-policy bits of the loads: from the coherent level
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(partial_slot2<NH>(pl, ws, T, 0), (short)0,
-                                                                         nc * NH * 1024, kRawBufferWord3);
-      f32x4 tot[NH];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) tot[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ci = 0; ci < nc; ++ci)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const f32x4 v = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((ci * NH + h) * 1024 + lane * 16), 0, kSc1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tot[h][e] += v[e];
-        }
-      store_tile2(rp, tot[0], pl.m, pl.n, T * 16 + j, g);
-      if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // owned slots restart at zero for the next round (after every wave has
-    // read them)
-    if (round + 1 < rounds) {
-      __syncthreads();
-      if (keeps)
-        for (int s2 = 2; s2 < OWN + 2; ++s2) slot_at(s2, 0, wave) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-}
-
-// Mixes of the second kernel: k = 3 and k = 2 with their pair tables.
-template <int BITS, int TAB> struct Mix2;
-template <> struct Mix2<4, kValueTable> { static constexpr int kMask = 0b00110011; };
-template <> struct Mix2<4, kCodeTable> { static constexpr int kMask = 0b00110011; };
-template <> struct Mix2<3, kPair3Table> { static constexpr int kMask = 0b11111111; };
-template <> struct Mix2<3, kValueTable> { static constexpr int kMask = 0b01010101; };
-template <> struct Mix2<3, kCodeTable> { static constexpr int kMask = 0b01010101; };
-template <> struct Mix2<2, kPairTable> { static constexpr int kMask = 0b11111111; };
-template <> struct Mix2<2, kValueTable> { static constexpr int kMask = 0b11110000; };
-template <> struct Mix2<2, kCodeTable> { static constexpr int kMask = 0b11110000; };
-
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -1907,87 +1304,6 @@ int table_override(int bits) {
   return t;
 }
 
-// Which prefill kernel later calls use (trellis_test_force_kernel): 0 the
-// library's choice, 1 prefill_kernel, 2 prefill2_kernel.
-std::atomic<int> g_force_kernel{0};
-
-// prefill2 plan; returns false if the table's LDS layout does not fit.
-bool make_plan2(int m, int n, int k, int cus, int tab, bool two, Plan2 &pl) {
-  pl = Plan2{};
-  pl.m = m;
-  pl.n = n;
-  pl.k = k;
-  pl.kb = k / 256;
-  pl.tiles = (n + 15) / 16;
-  const int64_t units = (int64_t)pl.tiles * pl.kb;  // <= 2^18 * 2^10
-  int64_t groups = units / kW2;
-  if (groups > cus) groups = cus;
-  if (groups < 1) groups = 1;
-  pl.groups = (int)groups;
-  pl.cq = (int)(units / groups);
-  pl.cr = (int)(units % groups);
-  pl.maxc = pl.kb / pl.cq + 2;
-  // table, then the per-wave sum slots (which hold the float16 code table
-  // while a pair table is built from it); as many owned tiles per round as
-  // the rest of the LDS holds, up to kOwnMax
-  pl.slot_lanes = 16 * (((m < 16 ? m : 16) + 3) / 4);
-  const int tb = table2_bytes(tab);
-  const int temp = tab == kPairTable || tab == kPair3Table ? kCodeTemp : 0;
-  const int per_slot = kW2 * pl.slot_lanes * 16;
-  int own = (kMaxLds - tb) / per_slot - 2;
-  if (own > kOwnMax) own = kOwnMax;
-  if (own < 1) return false;
-  pl.own = own;
-  int sb = (own + 2) * per_slot;
-  if (sb < temp) sb = temp;
-  pl.slots_off = tb;
-  pl.lds_bytes = tb + sb;
-  return pl.lds_bytes <= kMaxLds;
-}
-
-// prefill2 kernels: (k, table, matrices).
-constexpr int kV2 = 5;  // k4 value, k3 pair3, k3 value, k2 pair, k2 code
-int v2_index(int bits, int tab) {
-  if (bits == 4) return 0;
-  if (bits == 3) return tab == kPair3Table ? 1 : 2;
-  return tab == kPairTable ? 3 : 4;
-}
-typedef void (*Prefill2Fn)(const uint32_t *, const uint16_t *, const uint32_t *, const uint16_t *, float *,
-                           uint32_t *, Plan2, RowPtrs);
-Prefill2Fn prefill2_fn(int v) {
-  switch (v) {
-    case 0: return &prefill2_kernel<4, Mix2<4, kValueTable>::kMask, kValueTable>;
-    case 1: return &prefill2_kernel<3, Mix2<3, kPair3Table>::kMask, kPair3Table>;
-    case 2: return &prefill2_kernel<3, Mix2<3, kValueTable>::kMask, kValueTable>;
-    case 3: return &prefill2_kernel<2, Mix2<2, kPairTable>::kMask, kPairTable>;
-    default: return &prefill2_kernel<2, Mix2<2, kCodeTable>::kMask, kCodeTable>;
-  }
-}
-bool g_lds2_set[kMaxDevices][kV2] = {};
-
-// Table of the second kernel: k = 4 the value table; k = 3 and k = 2 their
-// pair tables when the LDS layout fits (one round of owned tiles per
-// workgroup for k = 3; not with two matrices and several rounds for k = 2),
-// else the value (k = 3) or code (k = 2) table. A forced table is used where
-// it exists for this kernel.
-int pick_table2(int m, int n, int k, int bits, int cus, bool two, Plan2 &pl) {
-  int order[3];
-  int cnt = 0;
-  const int forced = g_force_table.load(std::memory_order_relaxed);
-  if (bits == 4) {
-    order[cnt++] = kValueTable;
-  } else if (bits == 3) {
-    if (forced == kValueTable || forced == kCodeTable) order[cnt++] = kValueTable;
-    else { order[cnt++] = kPair3Table; order[cnt++] = kValueTable; }
-  } else {
-    if (forced == kValueTable || forced == kCodeTable) order[cnt++] = kCodeTable;
-    else { order[cnt++] = kPairTable; order[cnt++] = kCodeTable; }
-  }
-  for (int i = 0; i < cnt; ++i)
-    if (make_plan2(m, n, k, cus, order[i], two, pl)) return order[i];
-  return -1;
-}
-
 // One launch of the layer on m <= 15 rows (any m >= 1 with a valid
 // geometry; the entry points restrict m to their regimes): x row i at
 // x_rows[i], output row i at out_rows[i]. With a second matrix (codes2,
@@ -2006,34 +1322,6 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
     const trellis_status rc0 = device_state(st0, variant_of(g.bits, kValueTable, two));
     if (rc0 != TRELLIS_OK) return rc0;
     cus = st0->cus;
-  }
-  if (g_force_kernel.load(std::memory_order_relaxed) == 2 && !noalloc && !two) {
-    Plan2 p2;
-    const int tab2 = pick_table2(m, g.n, g.k, g.bits, cus, two, p2);
-    if (tab2 >= 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRELLIS_E_HIP;
-      const int v2 = v2_index(g.bits, tab2);
-      if (!g_lds2_set[dev][v2]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(prefill2_fn(v2)),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) != hipSuccess)
-          return TRELLIS_E_HIP;
-        g_lds2_set[dev][v2] = true;
-      }
-      Workspace *w = nullptr;
-      const size_t slot_floats = (size_t)p2.tiles * p2.maxc * 256 * (two ? 2 : 1);
-      const trellis_status rcw = workspace(stream, slot_floats, (size_t)p2.tiles, w);
-      if (rcw != TRELLIS_OK) return rcw;
-      RowPtrs rp2{};
-      for (int i = 0; i < kMaxRows; ++i) {
-        rp2.x[i] = x_rows[i < m ? i : 0];
-        rp2.out[i] = out_rows[i < m ? i : 0];
-      }
-      clear_last_error();
-      hipLaunchKernelGGL(prefill2_fn(v2), dim3((unsigned)p2.groups), dim3(kThreads2), p2.lds_bytes, stream, codes,
-                         scales_bf16, codes2, scales2, w->ws, w->counters, p2, rp2);
-      return launch_status();
-    }
   }
   // The table that splits x into the fewest K panels; among equals the pair
   // table (k = 2), then the value table. TRELLIS_TABLE overrides the choice.
@@ -2212,11 +1500,6 @@ trellis_status trellis_prefill_noalloc(const uint16_t *x_bf16, int32_t m, const 
     orow[i] = out_bf16 + (size_t)i * g.n;
   }
   return launch_rows(xr, orow, m, codes, scales_bf16, nullptr, nullptr, g, stream, true);
-}
-
-int trellis_test_force_kernel(int kind) {
-  if (kind < 0 || kind > 2) return -2;
-  return g_force_kernel.exchange(kind);
 }
 
 int trellis_test_force_table(int kind) {
