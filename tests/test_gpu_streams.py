@@ -9,7 +9,10 @@ it runs on or on what runs next to it. These tests hold the library to that:
   one after another on one stream;
 * a call captured into a HIP graph and replayed (with new inputs copied into
   the captured buffers, eager calls and synchronisations between replays)
-  gives, at every replay, the bits of the eager call on the same inputs.
+  gives, at every replay, the bits of the eager call on the same inputs;
+* two host threads calling at the same time with hipStreamPerThread (one
+  handle, a different stream per thread, so a workspace per thread) get the
+  one-stream bits.
 
 Shapes are chosen so that tiles are shared across workgroups (the wide
 geometry) and across K panels (M = 15, K = 17408), where the workspace and
@@ -121,3 +124,57 @@ def test_graph_capture_replay(case):
         torch.cuda.synchronize()
         assert np.array_equal(got, eager), f"{case}: replay {rep} differs from the eager call"
         check_against_oracle(got, x, codes, scales, k, bits, 7400 + rep, f"{case} replay {rep}")
+
+
+HIP_STREAM_PER_THREAD = 2  # hipStreamPerThread: the calling host thread's own default stream
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "m%d_k%d_n%d_b%d" % c)
+def test_per_thread_default_stream_from_two_threads(case):
+    # hipStreamPerThread is one handle that names a different stream on every
+    # host thread. Two threads calling with it at the same time run
+    # concurrently on the GPU, so each needs its own workspace; sharing one
+    # would race on the tile counters and partials. Both threads' results
+    # must equal the one-stream results bit for bit.
+    import threading
+
+    import torch
+
+    m, k, n, bits = case
+    print(f"per-thread default stream {case}", flush=True)
+    sets = [inputs(case, seed=7500 + 19 * i + m) for i in range(4)]
+    ref = []
+    for i, (x, codes, scales, dev) in enumerate(sets):
+        out = tp.prefill(*dev, bits)
+        torch.cuda.synchronize()
+        ref.append(from_dev_bf16(out))
+        check_against_oracle(ref[-1], x, codes, scales, k, bits, 7600 + i, f"{case} set {i}")
+    g = tp.geom(n, k, bits)
+    rounds = 6
+    outs = [[torch.empty((m, n), dtype=torch.bfloat16, device=sets[0][3][0].device) for _ in range(rounds)]
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    start = threading.Barrier(2)
+    errors = []
+
+    def worker(t):
+        try:
+            start.wait()
+            for r in range(rounds):
+                xd, cd, sd = sets[(t + r) % len(sets)][3]
+                tp.prefill_raw(xd.data_ptr(), m, cd.data_ptr(), sd.data_ptr(), g, outs[t][r].data_ptr(),
+                               HIP_STREAM_PER_THREAD)
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(2):
+        for r in range(rounds):
+            got = from_dev_bf16(outs[t][r])
+            assert np.array_equal(got, ref[(t + r) % len(sets)]), f"{case}: thread {t}, call {r} differs"
