@@ -164,6 +164,10 @@ def test_per_thread_default_stream_from_two_threads(case):
                 xd, cd, sd = sets[(t + r) % len(sets)][3]
                 tp.prefill_raw(xd.data_ptr(), m, cd.data_ptr(), sd.data_ptr(), g, outs[t][r].data_ptr(),
                                HIP_STREAM_PER_THREAD)
+            # Wait here, while the thread and its per-thread stream exist: a
+            # synchronisation after the thread has ended need not cover the
+            # work of the stream it leaves behind.
+            torch.cuda.synchronize()
         except Exception as e:  # reported below, in the test's own thread
             errors.append(e)
 

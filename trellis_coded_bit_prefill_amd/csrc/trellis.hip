@@ -430,14 +430,17 @@ __device__ __forceinline__ void unit_group(const LaneWords<BITS> &L, const unsig
 // wave waits out the LDS latency. The phased order was measured 2% faster
 // per launch (the same treatment of the k = 3 and k = 2 mixes gained
 // nothing). The LDS wait counter saturates past 15 outstanding reads, so
-// each phase issues its reads first and waits once, after the ALU work.
-template <int TAB, int U>
+// each phase waits once, after its ALU work. Within a phase the 16 gathers
+// go out four at a time between quarters of the ALU work rather than in one
+// burst: with 16 waves sharing the LDS, bursts queue behind each other, and
+// spreading them was measured 2-2.5% faster per launch at k = 4.
+template <int TAB, int U, int Q0 = 0, int Q1 = 4>
 __device__ __forceinline__ void span4_issue(const LaneWords<4> &L, const unsigned char *table, uint32_t mask,
                                             uint32_t (&r)[2][8]) {
   using R = TableRead<TAB>;
   constexpr int SH = R::kShift;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = Q0; i < Q1; ++i) {
     uint32_t a[4];
     switch (i) {
       case 0: quad_xa<(63 - (8 * U + 12 + 0)) * 4, SH>(L.d, mask, a); break;
@@ -459,9 +462,34 @@ __device__ __forceinline__ bf16x8 span4_weights(const uint32_t (&r)[8], float s,
   for (int e = 0; e < 8; ++e) w[e] = (__bf16)R::from_raw(r[e], s, q);
   return w;
 }
-template <int U>
-__device__ __forceinline__ bf16x8 alu4_weights(const LaneWords<4> &L, float q, float k) {
-  return group_alu<4, U>(L, q, k, std::make_integer_sequence<int, 8>{});
+// ALU-path weights S of group U (float32, before the bf16 rounding).
+template <int U, int... S>
+__device__ __forceinline__ void alu4_part(const LaneWords<4> &L, float q, float k, float (&f)[8],
+                                          std::integer_sequence<int, S...>) {
+  ((f[S] = __builtin_fmaf(code_plus_magic(win12<(63 - 8 * U - S) * 4>(L.d)), q, k)), ...);
+}
+__device__ __forceinline__ bf16x8 pack8(const float (&f)[8]) {
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = (__bf16)f[i];
+  return w;
+}
+// One ALU group of k = 4 in two quarters of the phase, each after a quad of
+// gathers (the gathers of quads Q and Q + 1 of the phase's table span).
+template <int TAB, int SPAN, int U, int Q>
+__device__ __forceinline__ bf16x8 alu4_between_gathers(const LaneWords<4> &L, const unsigned char *table,
+                                                       uint32_t mask, uint32_t (&r)[2][8], float q, float k) {
+  float f[8];
+  span4_issue<TAB, SPAN, Q, Q + 1>(L, table, mask, r);
+  __builtin_amdgcn_sched_barrier(0);
+  alu4_part<U>(L, q, k, f, std::integer_sequence<int, 0, 1, 2, 3>{});
+  __builtin_amdgcn_sched_barrier(0);
+  span4_issue<TAB, SPAN, Q + 1, Q + 2>(L, table, mask, r);
+  __builtin_amdgcn_sched_barrier(0);
+  alu4_part<U>(L, q, k, f, std::integer_sequence<int, 4, 5, 6, 7>{});
+  const bf16x8 w = pack8(f);
+  __builtin_amdgcn_sched_barrier(0);
+  return w;
 }
 __device__ __forceinline__ bf16x8 xop(const unsigned char *xa, int u) {
   return *reinterpret_cast<const bf16x8 *>(xa + 16 * u);
@@ -474,16 +502,13 @@ __device__ __forceinline__ void unit4_phased(const LaneWords<4> &L, const unsign
                                              const unsigned char *xa, float s, float q, float k, uint32_t mask,
                                              f32x4 &acc) {
   uint32_t r[2][8];
-  // Two phases: the x operands and the gathers of one table span are
-  // issued, two ALU groups run while they are in flight, and only then are
-  // the gathered entries turned into weights.
+  // Two phases: the x operands of the phase are read, the gathers of one
+  // table span go out a quad at a time between the quarters of two ALU
+  // groups, and only then are the gathered entries turned into weights.
   {
     const bf16x8 x2 = xop(xa, 2), x6 = xop(xa, 6), x0 = xop(xa, 0), x1 = xop(xa, 1);
-    span4_issue<TAB, 0>(L, table, mask, r);
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 w2 = alu4_weights<2>(L, q, k);
-    const bf16x8 w6 = alu4_weights<6>(L, q, k);
-    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 w2 = alu4_between_gathers<TAB, 0, 2, 0>(L, table, mask, r, q, k);
+    const bf16x8 w6 = alu4_between_gathers<TAB, 0, 6, 2>(L, table, mask, r, q, k);
     mfma(x2, w2, acc);
     mfma(x6, w6, acc);
     mfma(x0, span4_weights<TAB>(r[0], s, q), acc);
@@ -492,11 +517,8 @@ __device__ __forceinline__ void unit4_phased(const LaneWords<4> &L, const unsign
   __builtin_amdgcn_sched_barrier(0);
   {
     const bf16x8 x3 = xop(xa, 3), x7 = xop(xa, 7), x4 = xop(xa, 4), x5 = xop(xa, 5);
-    span4_issue<TAB, 4>(L, table, mask, r);
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 w3 = alu4_weights<3>(L, q, k);
-    const bf16x8 w7 = alu4_weights<7>(L, q, k);
-    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 w3 = alu4_between_gathers<TAB, 4, 3, 0>(L, table, mask, r, q, k);
+    const bf16x8 w7 = alu4_between_gathers<TAB, 4, 7, 2>(L, table, mask, r, q, k);
     mfma(x3, w3, acc);
     mfma(x7, w7, acc);
     mfma(x4, span4_weights<TAB>(r[0], s, q), acc);
@@ -1324,7 +1346,8 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
     cus = st0->cus;
   }
   // The table that splits x into the fewest K panels; among equals the pair
-  // table (k = 2), then the value table. TRELLIS_TABLE overrides the choice.
+  // table (k = 2), then the value table. The test hook (trellis_test_force_table)
+  // overrides the choice.
   int tab = kValueTable;
   Plan pl = make_plan(m, g.n, g.k, cus, table_bytes(kValueTable), two);
   const int forced = table_override(g.bits);
