@@ -27,9 +27,36 @@ def _device_asm() -> str:
             return f.read()
 
 
-@pytest.mark.skipif(not os.path.exists(_build.hipcc()), reason="hipcc not available")
-def test_prefill_kernels_use_no_scratch_and_fit_four_waves_per_simd():
-    asm = _device_asm()
+needs_hipcc = pytest.mark.skipif(not os.path.exists(_build.hipcc()), reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm():
+    return _device_asm()
+
+
+def _kernels(asm):
+    for blk in re.split(r"\n(?=_Z\S*:)", asm):
+        name = blk.split(":", 1)[0]
+        if "prefill_kernel" in name:
+            yield name, blk
+
+
+def _basic_blocks(blk):
+    """Instruction mnemonics of each basic block of a kernel's assembly."""
+    out, cur = [], None
+    for line in blk.split("\n"):
+        t = line.strip()
+        if re.match(r"^(\.LBB\S+|; %bb\.\d+):", t):
+            cur = []
+            out.append(cur)
+        elif cur is not None and t and not t.startswith((".", ";")):
+            cur.append(t.split()[0])
+    return out
+
+
+@needs_hipcc
+def test_prefill_kernels_use_no_scratch_and_fit_four_waves_per_simd(asm):
     # Each kernel's report follows its symbol: ".section ... <name>:" ...
     # "; ScratchSize: N" ... "; NumVgprs: N".
     blocks = re.split(r"\n(?=_Z\S*:)", asm)
@@ -46,3 +73,39 @@ def test_prefill_kernels_use_no_scratch_and_fit_four_waves_per_simd():
     # k = 2, 3, 4 x (value, code table) + the pair table, each for one matrix
     # and for the fused gate and up projections
     assert seen == 14, f"expected 14 prefill kernels, found {seen}"
+
+
+@needs_hipcc
+def test_bf16_rounding_of_weights_uses_the_packed_convert(asm):
+    # Every decoded weight is rounded from float32 to bf16 (round to nearest
+    # even) before it enters the MFMA. gfx950 rounds two per instruction
+    # (v_cvt_pk_bf16_f32); a software rounding (bias 0x7fff plus the lsb,
+    # then a shift) would cost several VALU ops per weight.
+    for name, blk in _kernels(asm):
+        assert blk.count("v_cvt_pk_bf16_f32") >= 32, f"{name}: no packed bf16 convert"
+        assert not re.search(r"v_add3_u32\S*\s.*0x7fff", blk), f"{name}: software bf16 rounding"
+
+
+@needs_hipcc
+def test_k4_unit_decode_instruction_budget(asm):
+    # The k = 4 one-matrix kernels decode a unit (16 rows x 256 weights; per
+    # lane 64 weights, 32 through the table and 32 through the hash on the
+    # ALU) in one basic block with 8 MFMAs: 32 table gathers and 8 x reads
+    # from LDS, and at most 292 VALU instructions (about 4.5 per weight:
+    # hash, byte sum, fused multiply-add or scale, window extraction, one
+    # packed convert per two weights). A regression here costs time on every
+    # unit without failing a parity test.
+    checked = 0
+    for name, blk in _kernels(asm):
+        if "prefill_kernelILi4ELi51ELi" not in name or "ELb0E" not in name:
+            continue
+        units = [b for b in _basic_blocks(blk) if b.count("v_mfma_f32_16x16x32_bf16") == 8
+                 and b.count("v_sad_u8") == 32]
+        assert units, f"{name}: no unit decode block found"
+        for b in units:
+            valu = sum(1 for m in b if m.startswith("v_"))
+            assert valu <= 292, f"{name}: {valu} VALU instructions per unit"
+            assert b.count("ds_read_b32") + b.count("ds_read_u16") == 32, f"{name}: table gathers"
+            assert b.count("ds_read_b128") == 8, f"{name}: x reads"
+        checked += 1
+    assert checked == 2  # value table and code table
