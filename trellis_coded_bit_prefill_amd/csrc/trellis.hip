@@ -134,7 +134,29 @@ struct Plan {
   int32_t x_contiguous;  // 1: x row i is at row 0 + i * K (plain calls); 0: per-row pointers
   int32_t slots_off;     // > 0: byte offset of dedicated partial-tile slots after x (LDS combine
                          // without barriers); 0: slots reuse the x region after a barrier
+  // Multipliers for exact division (div_by) by the divisors that locating a
+  // unit's piece needs: [0] cq + 1, [1] cq, [2] base + 1 and [3] base of a
+  // workgroup with cq + 1 units, [4] and [5] the same with cq units.
+  uint32_t dm[6];
+  uint32_t dl;  // their shifts l, 5 bits each (l = 0: the divisor is 1)
 };
+
+// n / d (unsigned, any 32-bit n) for a divisor whose multiplier the host
+// computed as m = floor(2^32 (2^l - d) / d) + 1 with l = ceil(log2 d): with
+// t = umulhi(n, m), n / d = (t + ((n - t) >> 1)) >> (l - 1). The round-up
+// multiplier method (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): a multiply-high, a subtract and
+// three shifts and adds on the scalar unit, where a division by a runtime
+// value would be a chain of about twenty instructions through the VALU's
+// reciprocal.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t l) {
+  const uint32_t t = __umulhi(n, m);
+  return l == 0 ? n : (t + ((n - t) >> 1)) >> ((l - 1) & 31u);
+}
+template <int I>
+__device__ __forceinline__ uint32_t div_by(uint32_t n, const Plan &pl) {
+  return div_magic(n, pl.dm[I], (pl.dl >> (5 * I)) & 31u);
+}
 
 // Split of a workgroup's contiguous units [u0, u0 + len) into s <= 16
 // pieces, one per wave. Wave slot w decodes the piece at position
@@ -154,7 +176,7 @@ __device__ __forceinline__ CuSplit cu_split(int c, const Plan &pl) {
   q.u0 = c * pl.cq + (c < pl.cr ? c : pl.cr);
   q.len = pl.cq + (c < pl.cr ? 1 : 0);
   q.s = q.len < kWaves ? q.len : kWaves;
-  q.base = q.s == kWaves ? q.len / kWaves : (int)((uint32_t)q.len / (uint32_t)q.s);
+  q.base = q.s == kWaves ? (int)((uint32_t)q.len / kWaves) : q.len > 0 ? 1 : 0;  // len / s
   const int r = q.len - q.base * q.s;
   q.ce = (r + 1) >> 1;
   q.h = r >> 1;
@@ -171,15 +193,18 @@ __device__ __forceinline__ int piece_start(const CuSplit &q, int p) {
 // consecutive pieces in unit order have consecutive indices.
 __device__ __forceinline__ int piece_of(int u, const Plan &pl) {
   const int cut = pl.cr * (pl.cq + 1);
-  const int c = u < cut ? (int)((uint32_t)u / (uint32_t)(pl.cq + 1))
-                        : pl.cr + (int)((uint32_t)(u - cut) / (uint32_t)pl.cq);
+  const int c = u < cut ? (int)div_by<0>((uint32_t)u, pl) : pl.cr + (int)div_by<1>((uint32_t)(u - cut), pl);
   const CuSplit q = cu_split(c, pl);
   const int o = u - q.u0;
   const int x1 = q.ce * (q.base + 1), x2 = x1 + (q.s - q.h - q.ce) * q.base;
+  // this workgroup's base + 1 and base (the divisors differ with its length)
+  const bool lng = c < pl.cr;
+  const uint32_t m1 = lng ? pl.dm[2] : pl.dm[4], l1 = (pl.dl >> (lng ? 10 : 20)) & 31u;
+  const uint32_t m0 = lng ? pl.dm[3] : pl.dm[5], l0 = (pl.dl >> (lng ? 15 : 25)) & 31u;
   int p;
-  if (o < x1) p = (int)((uint32_t)o / (uint32_t)(q.base + 1));
-  else if (o < x2) p = q.ce + (int)((uint32_t)(o - x1) / (uint32_t)q.base);
-  else p = q.s - q.h + (int)((uint32_t)(o - x2) / (uint32_t)(q.base + 1));
+  if (o < x1) p = (int)div_magic((uint32_t)o, m1, l1);
+  else if (o < x2) p = q.ce + (int)div_magic((uint32_t)(o - x1), m0, l0);
+  else p = q.s - q.h + (int)div_magic((uint32_t)(o - x2), m1, l1);
   return c * kWaves + p;
 }
 
@@ -1231,6 +1256,20 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   pl.groups = groups;
   pl.cq = pl.units / groups;
   pl.cr = pl.units % groups;
+  {
+    // Multipliers of div_by: l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+    auto base_of = [](uint32_t len) -> uint32_t { return len >= kWaves ? len / kWaves : len > 0 ? 1 : 0; };
+    const uint32_t bl = base_of((uint32_t)pl.cq + 1), bs = base_of((uint32_t)pl.cq);
+    const uint32_t divisors[6] = {(uint32_t)pl.cq + 1, (uint32_t)pl.cq, bl + 1, bl, bs + 1, bs};
+    pl.dl = 0;
+    for (int i = 0; i < 6; ++i) {
+      const uint32_t d = divisors[i];
+      uint32_t l = 0;
+      while ((1ull << l) < d) ++l;
+      pl.dm[i] = d <= 1 ? 0u : (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+      pl.dl |= (d <= 1 ? 0u : l) << (5 * i);
+    }
+  }
   // Pieces sharing one tile (per panel): at most (kp - 1) / (shortest piece) + 2.
   const int s_min = pl.cq < kWaves ? pl.cq : kWaves;
   pl.maxc = (pl.kp - 1) / (pl.cq / s_min) + 2;
