@@ -677,7 +677,9 @@ __device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, f32x4 
       uint16_t bits;
       if constexpr (TWO) bits = gate_up_bits(v[e], v2[e]);
       else bits = __builtin_bit_cast(uint16_t, (__bf16)v[e]);
-      reinterpret_cast<uint16_t *>(my_rows[e])[col] = bits;
+      // A global (not flat) store: a flat store might address LDS, so the
+      // compiler would make every later LDS read wait for its completion.
+      reinterpret_cast<__attribute__((address_space(1))) uint16_t *>(my_rows[e])[col] = bits;
     }
 }
 
