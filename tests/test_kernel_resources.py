@@ -109,3 +109,29 @@ def test_k4_unit_decode_instruction_budget(asm):
             assert b.count("ds_read_b128") == 8, f"{name}: x reads"
         checked += 1
     assert checked == 2  # value table and code table
+
+
+@needs_hipcc
+def test_inline_asm_stores_wait_out_mfma_and_sgpr_hazards(asm):
+    # The partial-tile stores are inline assembly, which the compiler's hazard
+    # recognizer does not look into: without the padding, a store could read
+    # an SGPR base address that a v_readlane (spill reload) wrote on the cycle
+    # before, or an accumulator an MFMA is still writing. Every such store
+    # (16 bytes, sc1) must follow at least 11 wait states of s_nop, directly
+    # or behind the first store of a pair.
+    seen = 0
+    for name, blk in _kernels(asm):
+        lines = [l.strip() for l in blk.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
+        for i, line in enumerate(lines):
+            if not (line.startswith("global_store_dwordx4") and "sc1" in line):
+                continue
+            seen += 1
+            k = i - 1
+            if lines[k].startswith("global_store_dwordx4"):
+                k -= 1
+            waits = 0
+            while k >= 0 and lines[k].startswith("s_nop"):
+                waits += int(lines[k].split()[1]) + 1
+                k -= 1
+            assert waits >= 11, f"{name}: {line} after {waits} wait states"
+    assert seen > 0

@@ -698,10 +698,16 @@ __device__ __forceinline__ float *partial_slot(const Plan &pl, float *ws, int ti
 // complete in order among themselves); the explicit s_waitcnt vmcnt(0) after
 // the main loop covers the store. sc1: written through to the level that is
 // coherent across the per-XCD L2s (agent scope). One 16-byte store per lane
-// keeps every write a whole cache line per wave; the s_nop covers the
-// store-data hazard of stores wider than 8 bytes.
+// keeps every write a whole cache line per wave. The compiler does not look
+// inside the asm for hazards on its inputs, so the leading s_nops give the
+// wait states a vector memory instruction needs after an MFMA wrote its data
+// (11 for an 8-pass MFMA) or a VALU wrote an SGPR it reads (5, such as a
+// v_readlane that reloads a spilled base address); the trailing s_nop covers
+// the store-data hazard of stores wider than 8 bytes.
+#define TRELLIS_ASM_VMEM_PAD "s_nop 7\n\ts_nop 4\n\t"
 __device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
   asm volatile(
+      TRELLIS_ASM_VMEM_PAD
       "global_store_dwordx4 %0, %1, off sc1\n\t"
       "s_nop 1"
       :
@@ -714,6 +720,7 @@ __device__ __forceinline__ void stage_partial(float *slot, f32x4 v) {
 // 32-bit lane offset, so nothing 64-bit per lane has to be kept live.
 __device__ __forceinline__ void stage_pair(float *base, uint32_t off, f32x4 v, f32x4 v2) {
   asm volatile(
+      TRELLIS_ASM_VMEM_PAD
       "global_store_dwordx4 %0, %1, %3 sc1\n\t"
       "global_store_dwordx4 %0, %2, %3 offset:1024 sc1\n\t"
       "s_nop 1"
