@@ -997,9 +997,22 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
   };
   // A tile finished inside the loop is never the range's last tile.
+  // The range's first tile, when it is shared with other workgroups and
+  // finished inside the loop, has its counter bumped one step after its
+  // partial was staged (the wave then waits for nothing but that step's code
+  // words); only the result is looked at after the loop. Counting it at the
+  // end instead would often make this wave, finishing its loop after the
+  // tile's other contributors, the last to arrive at two tiles, adding a
+  // round trip at the end of the launch.
+  bool bump_tf = false, tf_bumped = false;
+  uint32_t tf_old = 0;  // lane 0: the counter before this wave's bump
   auto tile_done = [&](int t, f32x4 v, f32x4 v2) {
-    if (cross(t)) stage(t, v, v2);
-    else if (t == tf && u0 > t * pl.kp) {
+    if (cross(t)) {
+      stage(t, v, v2);
+      // (several K panels only, where every tile is shared; two matrices:
+      // no VGPR to spare for the result)
+      if constexpr (!TWO) bump_tf = t == tf && pl.panels > 1;
+    } else if (t == tf && u0 > t * pl.kp) {
       if (pl.slots_off > 0) contribute(t, v, v2, 0);
       else if constexpr (TWO) stage_pair(kept_base, (uint32_t)lane * 16, v, v2);
       else part_f = v;
@@ -1024,6 +1037,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       constexpr bool kUp = decltype(second)::value;
       f32x4 &A = kUp ? acc2 : acc;
       if constexpr (!kUp) {
+        if (bump_tf) {
+          // The staged partial is complete before the counter moves.
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (lane == 0) tf_old = __hip_atomic_fetch_add(&counters[tf], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          bump_tf = false;
+          tf_bumped = true;
+        }
         if (tile != cur) {
           tile_done(cur, acc, acc2);
           cur = tile;
@@ -1115,7 +1135,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       uint32_t old = 0;
       if (mine) {
         contrib = piece_of((t + 1) * pl.kp - 1, pl) - piece_of(t * pl.kp, pl) + 1;
-        old = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == tf && tf_bumped) old = tf_old;  // counted inside the loop
+        else old = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       uint64_t last = __ballot(mine && old == (uint32_t)(contrib * pl.panels - 1));
       while (last) {
