@@ -139,6 +139,12 @@ struct Plan {
   // workgroup with cq + 1 units, [4] and [5] the same with cq units.
   uint32_t dm[6];
   uint32_t dl;  // their shifts l, 5 bits each (l = 0: the divisor is 1)
+  // Tile t's counter is word t << cshift of the counter array: 64 bytes
+  // apart for allocated workspaces, so the atomics on different tiles at the
+  // end of a launch do not queue behind each other on one cache line
+  // (measured 0.2 us per launch at M = 15, K = 17408), and packed (0) in the
+  // fixed scratch of the no-allocation entry point.
+  int32_t cshift;
 };
 
 // n / d (unsigned, any 32-bit n) for a divisor whose multiplier the host
@@ -1040,7 +1046,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         if (bump_tf) {
           // The staged partial is complete before the counter moves.
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          if (lane == 0) tf_old = __hip_atomic_fetch_add(&counters[tf], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) tf_old = __hip_atomic_fetch_add(&counters[(size_t)tf << pl.cshift], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           bump_tf = false;
           tf_bumped = true;
         }
@@ -1136,7 +1142,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       if (mine) {
         contrib = piece_of((t + 1) * pl.kp - 1, pl) - piece_of(t * pl.kp, pl) + 1;
         if (t == tf && tf_bumped) old = tf_old;  // counted inside the loop
-        else old = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else old = __hip_atomic_fetch_add(&counters[(size_t)t << pl.cshift], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       uint64_t last = __ballot(mine && old == (uint32_t)(contrib * pl.panels - 1));
       while (last) {
@@ -1147,7 +1153,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         f32x4 sum[NH];
         sum_partials<NH>(pl, ws, T, c, lane, sum);
         store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
-        if (lane == 0) __hip_atomic_store(&counters[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(&counters[(size_t)T << pl.cshift], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -1552,9 +1558,11 @@ trellis_status launch_rows(const uint16_t *const *x_rows, uint16_t *const *out_r
     if (two || (slot_floats + kept_floats) * 4 > kScratchBytes - kScratchCounterBytes) return TRELLIS_E_SCRATCH;
     counters = reinterpret_cast<uint32_t *>(st->scratch);
     ws = reinterpret_cast<float *>(st->scratch + kScratchCounterBytes);
+    pl.cshift = 0;
   } else {
     Workspace *w = nullptr;
-    rc = workspace(stream, slot_floats + kept_floats, (size_t)pl.tiles, w);
+    pl.cshift = 4;
+    rc = workspace(stream, slot_floats + kept_floats, (size_t)pl.tiles << pl.cshift, w);
     if (rc != TRELLIS_OK) return rc;
     ws = w->ws;
     counters = w->counters;
