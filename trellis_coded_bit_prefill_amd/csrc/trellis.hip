@@ -522,11 +522,28 @@ __device__ __forceinline__ bf16x8 alu4_between_gathers(const LaneWords<4> &L, co
   __builtin_amdgcn_sched_barrier(0);
   return w;
 }
+// A workgroup barrier for data in LDS only: the wave's LDS accesses are
+// complete when it arrives, while its global loads may still be in flight
+// (the compiler's barrier waits for those too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ bf16x8 xop(const unsigned char *xa, int u) {
   return *reinterpret_cast<const bf16x8 *>(xa + 16 * u);
 }
 __device__ __forceinline__ void mfma(bf16x8 xv, bf16x8 w, f32x4 &acc) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w, acc, 0, 0, 0);
+}
+template <int TAB>
+__device__ __forceinline__ void unit4_phase2(const LaneWords<4> &L, const unsigned char *table,
+                                             const unsigned char *xa, float s, float q, float k, uint32_t mask,
+                                             f32x4 &acc) {
+  uint32_t r[2][8];
+  const bf16x8 x3 = xop(xa, 3), x7 = xop(xa, 7), x4 = xop(xa, 4), x5 = xop(xa, 5);
+  const bf16x8 w3 = alu4_between_gathers<TAB, 4, 3, 0>(L, table, mask, r, q, k);
+  const bf16x8 w7 = alu4_between_gathers<TAB, 4, 7, 2>(L, table, mask, r, q, k);
+  mfma(x3, w3, acc);
+  mfma(x7, w7, acc);
+  mfma(x4, span4_weights<TAB>(r[0], s, q), acc);
+  mfma(x5, span4_weights<TAB>(r[1], s, q), acc);
 }
 template <int TAB>
 __device__ __forceinline__ void unit4_phased(const LaneWords<4> &L, const unsigned char *table,
@@ -546,15 +563,19 @@ __device__ __forceinline__ void unit4_phased(const LaneWords<4> &L, const unsign
     mfma(x1, span4_weights<TAB>(r[1], s, q), acc);
   }
   __builtin_amdgcn_sched_barrier(0);
-  {
-    const bf16x8 x3 = xop(xa, 3), x7 = xop(xa, 7), x4 = xop(xa, 4), x5 = xop(xa, 5);
-    const bf16x8 w3 = alu4_between_gathers<TAB, 4, 3, 0>(L, table, mask, r, q, k);
-    const bf16x8 w7 = alu4_between_gathers<TAB, 4, 7, 2>(L, table, mask, r, q, k);
-    mfma(x3, w3, acc);
-    mfma(x7, w7, acc);
-    mfma(x4, span4_weights<TAB>(r[0], s, q), acc);
-    mfma(x5, span4_weights<TAB>(r[1], s, q), acc);
-  }
+  unit4_phase2<TAB>(L, table, xa, s, q, k, mask, acc);
+}
+// The first phase's weights alone (groups 2, 6, 0, 1, in the order the
+// phase multiplies them), for a unit decoded before its x operands are in
+// LDS.
+template <int TAB>
+__device__ __forceinline__ void unit4_phase1_weights(const LaneWords<4> &L, const unsigned char *table, float s,
+                                                     float q, float k, uint32_t mask, bf16x8 (&w)[4]) {
+  uint32_t r[2][8];
+  w[0] = alu4_between_gathers<TAB, 0, 2, 0>(L, table, mask, r, q, k);
+  w[1] = alu4_between_gathers<TAB, 0, 6, 2>(L, table, mask, r, q, k);
+  w[2] = span4_weights<TAB>(r[0], s, q);
+  w[3] = span4_weights<TAB>(r[1], s, q);
 }
 
 // k = 2 with groups 0, 1 and 4, 5 on the table (windows of groups U and
@@ -618,6 +639,19 @@ __device__ __forceinline__ bf16x8 alu2_between_gathers(const LaneWords<2> &L, co
   return w;
 }
 template <int TAB>
+__device__ __forceinline__ void unit2_phase2(const LaneWords<2> &L, const unsigned char *table,
+                                             const unsigned char *xa, float s, float q, float k, uint32_t mask,
+                                             f32x4 &acc) {
+  uint32_t r[2][8];
+  const bf16x8 x3 = xop(xa, 3), x7 = xop(xa, 7), x4 = xop(xa, 4), x5 = xop(xa, 5);
+  const bf16x8 w3 = alu2_between_gathers<TAB, 4, 3, 0>(L, table, mask, r, q, k);
+  const bf16x8 w7 = alu2_between_gathers<TAB, 4, 7, 2>(L, table, mask, r, q, k);
+  mfma(x3, w3, acc);
+  mfma(x7, w7, acc);
+  mfma(x4, span4_weights<TAB>(r[0], s, q), acc);
+  mfma(x5, span4_weights<TAB>(r[1], s, q), acc);
+}
+template <int TAB>
 __device__ __forceinline__ void unit2_phased(const LaneWords<2> &L, const unsigned char *table,
                                              const unsigned char *xa, float s, float q, float k, uint32_t mask,
                                              f32x4 &acc) {
@@ -632,15 +666,16 @@ __device__ __forceinline__ void unit2_phased(const LaneWords<2> &L, const unsign
     mfma(x1, span4_weights<TAB>(r[1], s, q), acc);
   }
   __builtin_amdgcn_sched_barrier(0);
-  {
-    const bf16x8 x3 = xop(xa, 3), x7 = xop(xa, 7), x4 = xop(xa, 4), x5 = xop(xa, 5);
-    const bf16x8 w3 = alu2_between_gathers<TAB, 4, 3, 0>(L, table, mask, r, q, k);
-    const bf16x8 w7 = alu2_between_gathers<TAB, 4, 7, 2>(L, table, mask, r, q, k);
-    mfma(x3, w3, acc);
-    mfma(x7, w7, acc);
-    mfma(x4, span4_weights<TAB>(r[0], s, q), acc);
-    mfma(x5, span4_weights<TAB>(r[1], s, q), acc);
-  }
+  unit2_phase2<TAB>(L, table, xa, s, q, k, mask, acc);
+}
+template <int TAB>
+__device__ __forceinline__ void unit2_phase1_weights(const LaneWords<2> &L, const unsigned char *table, float s,
+                                                     float q, float k, uint32_t mask, bf16x8 (&w)[4]) {
+  uint32_t r[2][8];
+  w[0] = alu2_between_gathers<TAB, 0, 2, 0>(L, table, mask, r, q, k);
+  w[1] = alu2_between_gathers<TAB, 0, 6, 2>(L, table, mask, r, q, k);
+  w[2] = span4_weights<TAB>(r[0], s, q);
+  w[3] = span4_weights<TAB>(r[1], s, q);
 }
 
 template <int BITS, int MASK, int TAB, bool EXACT, int... U>
@@ -853,10 +888,15 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // slots: the unit being decoded and the next one in flight. The loop below
   // is unrolled by two so the slots alternate without copying registers that
   // still have loads pending. With two matrices slot 0 always holds a gate
-  // block and slot 1 the same block of up.
+  // block and slot 1 the same block of up. A decode-ahead prologue
+  // (below) requests two units and leaves the second for the loop in slot 0.
+  constexpr bool kAhead = !TWO && MASK == 0x33 && TAB != kPairTable && (BITS == 4 || BITS == 2);
   struct Slot {
     LaneWords<BITS> w;
-    uint32_t scb;  // raw bf16 scale bits
+    // raw bf16 scale bits (16 bits with the decode-ahead below: the second
+    // unit's scale crosses a barrier there, and widened to 32 bits it was
+    // waited for before the barrier)
+    std::conditional_t<kAhead, uint16_t, uint32_t> scb;
   };
   Slot S0, S1;
   int tile = (int)((uint32_t)u0 / (uint32_t)pl.kp);
@@ -882,6 +922,14 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // Prologue. x[:, panel] (M rows) is requested first, then the first unit's code words (memory-counter waits are in
   // issue order, so x can be stored to LDS without waiting for the codes);
   // the decode table is built while both are in flight.
+  // With the two-phase decodes (k = 4 and k = 2 on a value or code table,
+  // one matrix) a barrier follows the table, the second unit is requested,
+  // and each wave decodes its first unit's first phase before the barrier
+  // that waits for x: waves whose x arrived early decode while the rest of
+  // the workgroup's x is still on its way.
+  constexpr uint32_t kMaskAddr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
+  bool ahead = false;  // the first unit's first phase is decoded (its row scales are in range)
+  bf16x8 aw[4];        // its weights
   const int vecs = panel_k / 8;
   const int xtotal = pl.m * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
   {
@@ -926,6 +974,11 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       for (int e = tid; e < 4096; e += kWgThreads)
         s_table[e] = __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)e)));
     }
+    if constexpr (kAhead) {
+      lds_barrier();  // the table is built
+      // the range's second unit (its first again when it holds one unit)
+      request(S1, std::false_type{});
+    }
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
       const int idx = r * kWgThreads + tid;
@@ -934,9 +987,22 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = xv[r];
       }
     }
+    if constexpr (kAhead) {
+      if (u1 - u0 >= 2) {
+        const float s = scale_of(S0.scb);
+        float q, kq;
+        alu_row_constants(s, q, kq);
+        if (__all(alu_scale_ok(s))) {
+          ahead = true;
+          if constexpr (BITS == 4) unit4_phase1_weights<TAB>(S0.w, table, s, q, kq, kMaskAddr, aw);
+          else unit2_phase1_weights<TAB>(S0.w, table, s, q, kq, kMaskAddr, aw);
+        }
+      }
+    }
   }
 
-  __syncthreads();
+  if constexpr (kAhead) lds_barrier();
+  else __syncthreads();
 
   // A-operand rows j >= M read row M - 1: they only feed output rows >= M,
   // which are never stored.
@@ -1097,6 +1163,34 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       else __builtin_amdgcn_s_setprio(1);
     };
     using UpInSlot1 = std::bool_constant<TWO>;
+    if constexpr (kAhead) {
+      if (u1 - u0 >= 2) {
+        // The range's first unit, its successor already requested into S1;
+        // it finishes no tile. Its first phase is decoded unless its row
+        // scales are out of range.
+        const unsigned char *xb = xa + b * 512;
+        if (ahead) {
+          const bf16x8 x2 = xop(xb, 2), x6 = xop(xb, 6), x0 = xop(xb, 0), x1 = xop(xb, 1);
+          mfma(x2, aw[0], acc);
+          mfma(x6, aw[1], acc);
+          mfma(x0, aw[2], acc);
+          mfma(x1, aw[3], acc);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (BITS == 4) unit4_phase2<TAB>(S0.w, table, xb, s, q, kq, mask_addr, acc);
+          else unit2_phase2<TAB>(S0.w, table, xb, s, q, kq, mask_addr, acc);
+        } else {
+          unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(S0.w, table, xb, s, q, kq, mask_addr, acc,
+                                                            std::make_integer_sequence<int, 8>{});
+        }
+        advance(tile, b);
+        ++u;
+        const int rem = u1 - u + (holds_cross && pl.panels == 1 ? 1 : 0);  // as at the end of a step
+        if (rem >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (rem == 2) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
+        S0 = S1;  // the loop starts from slot 0 (one copy of the words, after their load)
+      }
+    }
     for (;;) {
       if constexpr (!TWO) {
         if (u + 1 == u1) {
