@@ -182,6 +182,29 @@ def test_prefill_each_table(bits, table, m, k, force_table):
     assert_prefill_close(out, y, a, f"table={table} m={m} k={k} bits={bits}")
 
 
+@pytest.mark.parametrize("bits,table", [(4, "value"), (4, "code"), (2, "value"), (2, "code")])
+@pytest.mark.parametrize("k", [256, 512])
+def test_prefill_ranges_of_one_and_two_units(bits, table, k, force_table):
+    # N = 65536 rows make 4096 tiles: on 256 workgroups of 16 waves every
+    # wave gets one unit with one K block (k = 256) and two with two. The
+    # two-phase kernels decode a range's first unit before the prologue's
+    # last barrier when the range holds two units or more and the unit's row
+    # scales are all inside the ALU path's exact range. Every fifth tile
+    # holds a scale of 2^115 and every tenth one of -2^-115, so first units
+    # take each branch, and one-unit ranges take the plain loop.
+    force_table(table)
+    m, n = 5, 65536
+    print(f"prefill one/two-unit ranges bits={bits} table={table} k={k}", flush=True)
+    x, codes, scales = generate(m, k, n, bits, seed=4500 + k + bits)
+    tiles = scales.reshape(-1, 16).copy()
+    tiles[::5, 3] = 0x7900
+    tiles[2::10, 7] = 0x8600
+    scales = tiles.reshape(-1)
+    out = gpu_prefill(x, codes, scales, bits)
+    y, a = oracle.prefill_parallel(x, codes, scales, k, bits)
+    assert_prefill_close(out, y, a, f"bits={bits} table={table} k={k}")
+
+
 def test_prefill_workspace_grows_between_calls():
     # One stream: a small call, a call needing a larger workspace (more tiles,
     # K panels), then the small call again; the grown workspace starts with
