@@ -698,19 +698,19 @@ __device__ __forceinline__ uint16_t gate_up_bits(float gate_sum, float up_sum) {
   return __builtin_bit_cast(uint16_t, (__bf16)(silu * up));
 }
 
-// Lane (j, g) holds rows 4g .. 4g+3 of output column `col`; the row
-// pointers come from the LDS copy of the row table. One matrix: v is the
+// Lane l holds rows 4 (l / 16) .. 4 (l / 16) + 3 of output column
+// col0 + l % 16; the row pointers come from the LDS copy of the row table. One matrix: v is the
 // tile's sum. Two (gate and up): v and v2 are the two projections' sums and
 // the output is the elementwise tail.
 template <bool TWO>
-__device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, f32x4 v2, int m, int ncols, int col,
-                                           int g) {
+__device__ __forceinline__ void store_tile(const uint64_t *rows, f32x4 v, f32x4 v2, int m, int ncols, int col0) {
+  // The lane's column and rows are formed here, from the lane id, at the
+  // store: the empty asm keeps the compiler from hoisting them out of the
+  // main loop, where keeping them live would spill.
+  int lane_id = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lane_id));
+  const int col = col0 + (lane_id & 15), gr = (lane_id >> 4) * 4;
   if (col >= ncols) return;
-  // The lane's row-table address is formed here, at the store: the empty
-  // asm keeps the compiler from hoisting it out of the main loop, where one
-  // more live register would spill.
-  int gr = 4 * g;
-  asm volatile("" : "+v"(gr));
   const uint64_t *my_rows = rows + gr;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // still have loads pending. With two matrices slot 0 always holds a gate
   // block and slot 1 the same block of up. A decode-ahead prologue
   // (below) requests two units and leaves the second for the loop in slot 0.
-  constexpr bool kAhead = !TWO && MASK == 0x33 && TAB != kPairTable && (BITS == 4 || BITS == 2);
+  constexpr bool kAhead = MASK == 0x33 && TAB != kPairTable && (BITS == 4 || BITS == 2);
   struct Slot {
     LaneWords<BITS> w;
     // raw bf16 scale bits (16 bits with the decode-ahead below: the second
@@ -922,11 +922,12 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // Prologue. x[:, panel] (M rows) is requested first, then the first unit's code words (memory-counter waits are in
   // issue order, so x can be stored to LDS without waiting for the codes);
   // the decode table is built while both are in flight.
-  // With the two-phase decodes (k = 4 and k = 2 on a value or code table,
-  // one matrix) a barrier follows the table, the second unit is requested,
-  // and each wave decodes its first unit's first phase before the barrier
-  // that waits for x: waves whose x arrived early decode while the rest of
-  // the workgroup's x is still on its way.
+  // With the two-phase decodes (k = 4 and k = 2 on a value or code table) a
+  // barrier follows the table, the second unit (with two matrices: the up
+  // block of the first) is requested, and each wave decodes the first phase
+  // of its first unit (gate block) before the barrier that waits for x:
+  // waves whose x arrived early decode while the rest of the workgroup's x
+  // is still on its way.
   constexpr uint32_t kMaskAddr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
   bool ahead = false;  // the first unit's first phase is decoded (its row scales are in range)
   bf16x8 aw[4];        // its weights
@@ -976,8 +977,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
     if constexpr (kAhead) {
       lds_barrier();  // the table is built
-      // the range's second unit (its first again when it holds one unit)
-      request(S1, std::false_type{});
+      // the range's second unit (its first again when it holds one unit);
+      // with two matrices the up block of the first unit
+      request(S1, std::bool_constant<TWO>{});
     }
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
@@ -1066,7 +1068,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         for (int e = 0; e < 4; ++e) sum[h][e] += w[e];
       }
     }
-    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
+    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16);
   };
   // A tile finished inside the loop is never the range's last tile.
   // The range's first tile, when it is shared with other workgroups and
@@ -1088,7 +1090,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       if (pl.slots_off > 0) contribute(t, v, v2, 0);
       else if constexpr (TWO) stage_pair(kept_base, (uint32_t)lane * 16, v, v2);
       else part_f = v;
-    } else store_tile<TWO>(s_rows, v, v2, pl.m, pl.n, t * 16 + j, g);
+    } else store_tile<TWO>(s_rows, v, v2, pl.m, pl.n, t * 16);
   };
   if (active) {
     int cur = tile;
@@ -1165,9 +1167,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     using UpInSlot1 = std::bool_constant<TWO>;
     if constexpr (kAhead) {
       if (u1 - u0 >= 2) {
-        // The range's first unit, its successor already requested into S1;
-        // it finishes no tile. Its first phase is decoded unless its row
-        // scales are out of range.
+        // The range's first unit (gate block), its successor (up block)
+        // already requested into S1; it finishes no tile. Its first phase is
+        // decoded unless its row scales are out of range.
         const unsigned char *xb = xa + b * 512;
         if (ahead) {
           const bf16x8 x2 = xop(xb, 2), x6 = xop(xb, 6), x0 = xop(xb, 0), x1 = xop(xb, 1);
@@ -1182,13 +1184,19 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
           unit<BITS, 0xFF, kValueTable, TAB != kValueTable>(S0.w, table, xb, s, q, kq, mask_addr, acc,
                                                             std::make_integer_sequence<int, 8>{});
         }
-        advance(tile, b);
-        ++u;
-        const int rem = u1 - u + (holds_cross && pl.panels == 1 ? 1 : 0);  // as at the end of a step
-        if (rem >= 3) __builtin_amdgcn_s_setprio(3);
-        else if (rem == 2) __builtin_amdgcn_s_setprio(2);
-        else __builtin_amdgcn_s_setprio(1);
-        S0 = S1;  // the loop starts from slot 0 (one copy of the words, after their load)
+        if constexpr (TWO) {
+          // the unit's up block (requesting the next unit's gate block into
+          // slot 0, where the loop starts)
+          step(S1, S0, std::false_type{}, UpInSlot1{});
+        } else {
+          advance(tile, b);
+          ++u;
+          const int rem = u1 - u + (holds_cross && pl.panels == 1 ? 1 : 0);  // as at the end of a step
+          if (rem >= 3) __builtin_amdgcn_s_setprio(3);
+          else if (rem == 2) __builtin_amdgcn_s_setprio(2);
+          else __builtin_amdgcn_s_setprio(1);
+          S0 = S1;  // the loop starts from slot 0 (one copy of the words, after their load)
+        }
       }
     }
     for (;;) {
@@ -1208,7 +1216,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     tl = cur;
     if (cross(cur)) stage(cur, acc, acc2);
     else if (u0 <= cur * pl.kp && u1 == (cur + 1) * pl.kp)
-      store_tile<TWO>(s_rows, acc, acc2, pl.m, pl.n, cur * 16 + j, g);
+      store_tile<TWO>(s_rows, acc, acc2, pl.m, pl.n, cur * 16);
     else if (pl.slots_off > 0) contribute(cur, acc, acc2, cur == tf ? 0 : 1);
     else if (cur == tf) {
       part_f = acc;
@@ -1246,7 +1254,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         const int c = __shfl(contrib, i);
         f32x4 sum[NH];
         sum_partials<NH>(pl, ws, T, c, lane, sum);
-        store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
+        store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16);
         if (lane == 0) __hip_atomic_store(&counters[(size_t)T << pl.cshift], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -1316,7 +1324,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       }
       if (e >= t1u) break;  // T ends in this segment
     }
-    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16 + j, g);
+    store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16);
   }
 }
 
