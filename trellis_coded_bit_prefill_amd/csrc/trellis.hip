@@ -923,11 +923,12 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // issue order, so x can be stored to LDS without waiting for the codes);
   // the decode table is built while both are in flight.
   // With the two-phase decodes (k = 4 and k = 2 on a value or code table) a
-  // barrier follows the table, the second unit (with two matrices: the up
-  // block of the first) is requested, and each wave decodes the first phase
-  // of its first unit (gate block) before the barrier that waits for x:
-  // waves whose x arrived early decode while the rest of the workgroup's x
-  // is still on its way.
+  // barrier follows the table, and each wave decodes the first phase of its
+  // first unit (gate block) before the barrier that waits for x: waves whose
+  // x arrived early decode while the rest of the workgroup's x is still on
+  // its way. The second unit (with two matrices: the up block of the first)
+  // is requested after that decode, so that it does not compete with x and
+  // the first unit's words.
   constexpr uint32_t kMaskAddr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
   bool ahead = false;  // the first unit's first phase is decoded (its row scales are in range)
   bf16x8 aw[4];        // its weights
@@ -977,9 +978,6 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
     if constexpr (kAhead) {
       lds_barrier();  // the table is built
-      // the range's second unit (its first again when it holds one unit);
-      // with two matrices the up block of the first unit
-      request(S1, std::bool_constant<TWO>{});
     }
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
@@ -1000,6 +998,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
           else unit2_phase1_weights<TAB>(S0.w, table, s, q, kq, kMaskAddr, aw);
         }
       }
+      // the range's second unit (its first again when it holds one unit);
+      // with two matrices the up block of the first unit
+      request(S1, std::bool_constant<TWO>{});
     }
   }
 
