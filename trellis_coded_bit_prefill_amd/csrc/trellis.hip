@@ -840,6 +840,14 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int j = lane & 15, g = lane >> 4;
+  // The lane id again, for the code after the prologue: formed where it is
+  // used (the empty asm keeps it there), so no register holds it through
+  // the main loop.
+  auto lane_id = []() {
+    int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   const int panel = blockIdx.x % pl.panels;
   const int group = blockIdx.x / pl.panels;
   const int panel_k = pl.kp * 256;
@@ -1031,7 +1039,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   f32x4 part_f2 = {0.f, 0.f, 0.f, 0.f}, part_l2 = {0.f, 0.f, 0.f, 0.f};
   float *const kept_base = kept + ((int64_t)blockIdx.x * kWaves + wave) * 512;  // wave-uniform
   auto stage = [&](int t, f32x4 v, f32x4 v2) {
-    float *slot = partial_slot<NH>(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane);
+    float *slot = partial_slot<NH>(pl, ws, t, panel, piece - piece_of(t * pl.kp, pl), lane_id());
     stage_partial(slot, v);
     if constexpr (TWO) stage_partial(slot + 256, v2);
   };
@@ -1043,6 +1051,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // completes before its counter update, and the last arriver reads only
   // after its own update returned, so it sees every partial.
   auto contribute = [&](int T, f32x4 v, f32x4 v2, int which) {
+    const int lane = lane_id();
     f32x4 *slots = reinterpret_cast<f32x4 *>(xl + pl.slots_off);  // [piece][first, last][matrix][lane]
     uint32_t *cnt = reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes);
     slots[((seg * 2 + which) * NH) * kWave + lane] = v;
@@ -1089,7 +1098,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       if constexpr (!TWO) bump_tf = t == tf && pl.panels > 1;
     } else if (t == tf && u0 > t * pl.kp) {
       if (pl.slots_off > 0) contribute(t, v, v2, 0);
-      else if constexpr (TWO) stage_pair(kept_base, (uint32_t)lane * 16, v, v2);
+      else if constexpr (TWO) stage_pair(kept_base, (uint32_t)lane_id() * 16, v, v2);
       else part_f = v;
     } else store_tile<TWO>(s_rows, v, v2, pl.m, pl.n, t * 16);
   };
@@ -1115,7 +1124,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         if (bump_tf) {
           // The staged partial is complete before the counter moves.
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          if (lane == 0) tf_old = __hip_atomic_fetch_add(&counters[(size_t)tf << pl.cshift], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane_id() == 0) tf_old = __hip_atomic_fetch_add(&counters[(size_t)tf << pl.cshift], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           bump_tf = false;
           tf_bumped = true;
         }
@@ -1228,6 +1237,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
   }
 
+  const int lane_post = lane_id();
   // ---- Publish the cross tiles of the range: once the staged partials are
   // complete, bump each tile's counter (one lane per tile); the contributor
   // that arrives last adds all partials in a fixed order (panel, then piece),
@@ -1238,7 +1248,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   if (holds_cross) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     for (int t0 = tf; t0 <= tl; t0 += kWave) {
-      const int t = t0 + lane;
+      const int t = t0 + lane_post;
       const bool mine = t <= tl && cross(t);
       int contrib = 0;
       uint32_t old = 0;
@@ -1254,9 +1264,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
         const int T = t0 + i;
         const int c = __shfl(contrib, i);
         f32x4 sum[NH];
-        sum_partials<NH>(pl, ws, T, c, lane, sum);
+        sum_partials<NH>(pl, ws, T, c, lane_post, sum);
         store_tile<TWO>(s_rows, sum[0], sum[NH - 1], pl.m, pl.n, T * 16);
-        if (lane == 0) __hip_atomic_store(&counters[(size_t)T << pl.cshift], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane_post == 0) __hip_atomic_store(&counters[(size_t)T << pl.cshift], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -1272,8 +1282,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       constexpr int kSc1 = 16;  // cache-policy bits of the loads
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(kept_base, (short)0, 2048, kRawBufferWord3);
-      part_f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)lane * 16, 0, kSc1));
-      part_f2 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 + (uint32_t)lane * 16, 0, kSc1));
+      part_f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)lane_post * 16, 0, kSc1));
+      part_f2 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 1024 + (uint32_t)lane_post * 16, 0, kSc1));
     }
   }
 
@@ -1284,11 +1294,11 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   __syncthreads();  // all waves are done reading x; its LDS holds the partials now
   f32x4 *slots = reinterpret_cast<f32x4 *>(xl);  // [segment][first, last][matrix][lane]
   if (active) {
-    slots[(seg * 2 + 0) * NH * kWave + lane] = part_f;
-    slots[(seg * 2 + 1) * NH * kWave + lane] = part_l;
+    slots[(seg * 2 + 0) * NH * kWave + lane_post] = part_f;
+    slots[(seg * 2 + 1) * NH * kWave + lane_post] = part_l;
     if constexpr (TWO) {
-      slots[((seg * 2 + 0) * NH + 1) * kWave + lane] = part_f2;
-      slots[((seg * 2 + 1) * NH + 1) * kWave + lane] = part_l2;
+      slots[((seg * 2 + 0) * NH + 1) * kWave + lane_post] = part_f2;
+      slots[((seg * 2 + 1) * NH + 1) * kWave + lane_post] = part_l2;
     }
   }
   __syncthreads();
@@ -1319,7 +1329,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       else break;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const f32x4 v = slots[((sidx * 2 + which_slot) * NH + h) * kWave + lane];
+        const f32x4 v = slots[((sidx * 2 + which_slot) * NH + h) * kWave + lane_post];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) sum[h][e2] += v[e2];
       }
