@@ -281,7 +281,7 @@ def main():
     ap.add_argument("--cpu-passes", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' figures")
     ap.add_argument("--extra-steps", type=int, default=300,
-                    help="timed steps per extra workload (after as many warm-up steps)")
+                    help="timed steps per extra workload (after --warmup warm-up steps)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -365,16 +365,20 @@ def main():
     if not args.no_extra and args.workload == WORKLOAD and not args.warm:
         # The other workloads of the metric (same cold protocol, their own
         # warm-up and timed steps), and the headline shape with one input set
-        # (codes resident in the 256 MB Infinity Cache), labelled warm.
+        # (codes resident in the 256 MB Infinity Cache), labelled warm. Each
+        # gets the full warm-up: its inputs are generated on the host first,
+        # the GPU idles meanwhile, and after a few hundred launches its clocks
+        # have not come back up (300 warm-up launches read about 2 us slow).
         extra = {}
         for name, warm in (("wide_m8_k3", False), ("wide_m15_k2", False), ("down_m15_k4", False),
                            ("wide_m5_k4", True)):
             w = Workload(SHAPES[name], warm)
-            ms, _ = w.timed(args.extra_steps, args.extra_steps)
+            ms, _ = w.timed(args.extra_steps, args.warmup)
             w.release()
             rec_x = summary(SHAPES[name], ms)
             rec_x["mode"] = "warm" if warm else "cold"
             rec_x["steps"] = args.extra_steps
+            rec_x["warmup"] = args.warmup
             p = profile_figures(name, sha)
             if p:
                 rec_x.update(p)
