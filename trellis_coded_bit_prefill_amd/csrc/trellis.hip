@@ -927,10 +927,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
       if (++pu < u1) advance(pt, pb);
     }
   };
-  // Prologue. x[:, panel] (M rows) is requested first, then the first
-  // unit's code words (memory-counter waits are in issue order, so x can be
-  // stored to LDS without waiting for the codes); the decode table is built
-  // while both are in flight.
+  // Prologue. x[:, panel] (M rows) is requested first, then the first unit's code words (memory-counter waits are in
+  // issue order, so x can be stored to LDS without waiting for the codes);
+  // the decode table is built while both are in flight.
   // With the two-phase decodes (k = 4 and k = 2 on a value or code table) a
   // barrier follows the table, and each wave decodes the first phase of its
   // first unit (gate block) before the barrier that waits for x: waves whose
