@@ -70,6 +70,7 @@ constexpr int kCombineBytes = kWaves * 2 * kWave * 16;  // LDS partial tiles of 
                                                         // (per matrix: twice that for gate and up)
 constexpr int kCombineCounters = kWaves * 4;             // LDS counters of the barrier-free combine
 static_assert(kStageRegs * kWgThreads * 16 >= kMaxLds - table_bytes(kCodeTable), "x staging must cover the largest panel");
+static_assert(kStageRegs * kWgThreads <= 32 << 9, "staged x vector indices divide by the row length with 9-bit quotients");
 
 // ---------------------------------------------------------------------------
 // trellis_decode: W[N, K] bf16. One thread per 8 consecutive weights of one
@@ -130,7 +131,7 @@ struct Plan {
                      // same block of both
   int32_t cq;        // units / groups: every workgroup gets cq or cq + 1 units
   int32_t cr;        // units % groups: the first cr workgroups get cq + 1
-  uint32_t xdiv;     // ceil(2^32 / (x vectors per staged row)), for exact division by umulhi
+  uint32_t xmul, xshift;  // row of a staged x vector idx: ((idx >> 5) * xmul) >> xshift
   int32_t x_contiguous;  // 1: x row i is at row 0 + i * K (plain calls); 0: per-row pointers
   int32_t slots_off;     // > 0: byte offset of dedicated partial-tile slots after x (LDS combine
                          // without barriers); 0: slots reuse the x region after a barrier
@@ -942,27 +943,39 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   bf16x8 aw[4];        // its weights
   const int vecs = panel_k / 8;
   const int xtotal = pl.m * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
+  // Staged x vector idx (16 B) is row i = idx / vecs, column idx - i * vecs;
+  // rows are one vector longer in LDS, so it lands at byte 16 (idx + i).
+  // A wave skips the rounds that start past the panel; lanes past it take
+  // the panel's last vector (a second load of it and an identical store).
+  auto xrow = [&](int idx) { return (int)(__umul24((uint32_t)idx >> 5, pl.xmul) >> pl.xshift); };
   {
     uint4 xv[kStageRegs];
 #pragma unroll
-    for (int r = 0; r < kStageRegs; ++r) {
-      const int idx = r * kWgThreads + tid;
-      xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
-      if (pl.x_contiguous) {
-        // Rows K elements apart from row 0: one base address.
-        if (idx < xtotal) {
-          const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
-          xv[r] = *reinterpret_cast<const uint4 *>(rp.x[0] + (int64_t)i * pl.k + kbase + 8 * c);
+    for (int r = 0; r < kStageRegs; ++r) xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
+    const int xlast = xtotal - 1;
+    if (pl.x_contiguous) {
+      // Rows K elements apart: vector idx is 16 (idx + i (panels - 1) vecs)
+      // bytes past row 0's part of the panel.
+      const unsigned char *const xb = reinterpret_cast<const unsigned char *>(rp.x[0] + kbase);
+      const uint32_t pstep = (uint32_t)((pl.panels - 1) * vecs);
+#pragma unroll
+      for (int r = 0; r < kStageRegs; ++r) {
+        if (r * kWgThreads + wave * kWave < xtotal) {
+          const int idx = min(r * kWgThreads + tid, xlast);
+          xv[r] = *reinterpret_cast<const uint4 *>(xb + ((uint32_t)idx + __umul24((uint32_t)xrow(idx), pstep)) * 16u);
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kStageRegs; ++r) {
+        if (r * kWgThreads + wave * kWave >= xtotal) continue;
         // A wave's 64 vectors start at a multiple of 64 and a row holds a
         // multiple of 32 of them, so they lie in rows i0 and i0 + 1 (uniform).
-        const int i0 = min((int)__umulhi((uint32_t)(r * kWgThreads + wave * kWave), pl.xdiv), kMaxRows - 2);
+        const int i0 = min(xrow(r * kWgThreads + wave * kWave), kMaxRows - 2);
         const uint16_t *const x0 = rp.x[i0], *const x1 = rp.x[i0 + 1];
-        if (idx < xtotal) {
-          const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
-          xv[r] = *reinterpret_cast<const uint4 *>((i == i0 ? x0 : x1) + kbase + 8 * c);
-        }
+        const int idx = min(r * kWgThreads + tid, xlast);
+        const int i = xrow(idx), c = idx - (int)__umul24((uint32_t)i, (uint32_t)vecs);
+        xv[r] = *reinterpret_cast<const uint4 *>((i == i0 ? x0 : x1) + kbase + 8 * c);
       }
     }
     if (wave == 0) {
@@ -989,11 +1002,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     }
 #pragma unroll
     for (int r = 0; r < kStageRegs; ++r) {
-      const int idx = r * kWgThreads + tid;
-      if (idx < xtotal) {
-        const int i = (int)__umulhi((uint32_t)idx, pl.xdiv), c = idx - i * vecs;
-        *reinterpret_cast<uint4 *>(xl + i * pl.x_stride + 16 * c) = xv[r];
-      }
+      if (r * kWgThreads + wave * kWave >= xtotal) continue;
+      const int idx = min(r * kWgThreads + tid, xlast);
+      *reinterpret_cast<uint4 *>(xl + 16 * (idx + xrow(idx))) = xv[r];
     }
     if constexpr (kAhead) {
       if (u1 - u0 >= 2) {
@@ -1401,11 +1412,15 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
   pl.panels = panels;
   pl.kp = kb / panels;
   pl.x_stride = pl.kp * 512 + 16;
-  // Staging divides a vector index (< 2^14) by the vectors per row
-  // (kp * 32 >= 32): umulhi(i, ceil(2^32 / d)) is exact while i * d < 2^32.
+  // Staging divides a vector index idx by the vectors per row (kp * 32):
+  // n = idx >> 5 < 2^9, and with l = ceil(log2 kp), m = ceil(2^(9 + l) / kp)
+  // (< 2^10) gives n / kp = (n * m) >> (9 + l) exactly (round-up multiplier,
+  // Granlund and Montgomery 1994), one 24-bit multiply on the VALU.
   {
-    const uint64_t d = (uint64_t)pl.kp * 32;
-    pl.xdiv = (uint32_t)(((1ull << 32) + d - 1) / d);
+    uint32_t l = 0;
+    while ((1u << l) < (uint32_t)pl.kp) ++l;
+    pl.xshift = 9 + l;
+    pl.xmul = (uint32_t)(((1ull << (9 + l)) + (uint32_t)pl.kp - 1) / (uint32_t)pl.kp);
   }
   int groups = cus / panels;
   if (groups < 1) groups = 1;
