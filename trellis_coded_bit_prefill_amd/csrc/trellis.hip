@@ -137,9 +137,10 @@ struct Plan {
                          // without barriers); 0: slots reuse the x region after a barrier
   // Multipliers for exact division (div_by) by the divisors that locating a
   // unit's piece needs: [0] cq + 1, [1] cq, [2] base + 1 and [3] base of a
-  // workgroup with cq + 1 units, [4] and [5] the same with cq units.
-  uint32_t dm[6];
-  uint32_t dl;  // their shifts l, 5 bits each (l = 0: the divisor is 1)
+  // workgroup with cq + 1 units, [4] and [5] the same with cq units; and by
+  // [6] panels and [7] kp (a workgroup's panel, a unit's tile).
+  uint32_t dm[8];
+  uint32_t dl, dl2;  // their shifts l, 5 bits each, [0..5] and [6..7] (l = 0: the divisor is 1)
   // Tile t's counter is word t << cshift of the counter array: 64 bytes
   // apart for allocated workspaces, so the atomics on different tiles at the
   // end of a launch do not queue behind each other on one cache line
@@ -162,7 +163,7 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t l
 }
 template <int I>
 __device__ __forceinline__ uint32_t div_by(uint32_t n, const Plan &pl) {
-  return div_magic(n, pl.dm[I], (pl.dl >> (5 * I)) & 31u);
+  return div_magic(n, pl.dm[I], ((I < 6 ? pl.dl : pl.dl2) >> (5 * (I % 6))) & 31u);
 }
 
 // Split of a workgroup's contiguous units [u0, u0 + len) into s <= 16
@@ -849,10 +850,54 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     asm volatile("" : "+v"(l));
     return l;
   };
-  const int panel = blockIdx.x % pl.panels;
-  const int group = blockIdx.x / pl.panels;
+  // Row 0's pointer is read with the plan (the empty asm keeps the read at
+  // the top, not in a branch below where it would wait on its own).
+  const uint16_t *const x_row0 = rp.x[0];
+  asm volatile("" ::"s"(x_row0));
+  const int group = (int)div_by<6>(blockIdx.x, pl);
+  const int panel = (int)blockIdx.x - group * pl.panels;
   const int panel_k = pl.kp * 256;
   const int64_t kbase = (int64_t)panel * panel_k;
+  // x[:, panel] is requested first: it needs only the panel, and every
+  // workgroup stages it before its first unit.
+  const int vecs = panel_k / 8;
+  const int xtotal = pl.m * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
+  // Staged x vector idx (16 B) is row i = idx / vecs, column idx - i * vecs;
+  // rows are one vector longer in LDS, so it lands at byte 16 (idx + i).
+  // A wave skips the rounds that start past the panel; lanes past it take
+  // the panel's last vector (a second load of it and an identical store).
+  auto xrow = [&](int idx) { return (int)(__umul24((uint32_t)idx >> 5, pl.xmul) >> pl.xshift); };
+  const int xlast = xtotal - 1;
+  uint4 xv[kStageRegs];
+  {
+#pragma unroll
+    for (int r = 0; r < kStageRegs; ++r) xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
+    const unsigned char *const xb = reinterpret_cast<const unsigned char *>(x_row0 + kbase);
+    if (pl.x_contiguous) {
+      // Rows K elements apart: vector idx is 16 (idx + i (panels - 1) vecs)
+      // bytes past row 0's part of the panel.
+      const uint32_t pstep = (uint32_t)((pl.panels - 1) * vecs);
+#pragma unroll
+      for (int r = 0; r < kStageRegs; ++r) {
+        if (r * kWgThreads + wave * kWave < xtotal) {
+          const int idx = min(r * kWgThreads + tid, xlast);
+          xv[r] = *reinterpret_cast<const uint4 *>(xb + ((uint32_t)idx + __umul24((uint32_t)xrow(idx), pstep)) * 16u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kStageRegs; ++r) {
+        if (r * kWgThreads + wave * kWave >= xtotal) continue;
+        // A wave's 64 vectors start at a multiple of 64 and a row holds a
+        // multiple of 32 of them, so they lie in rows i0 and i0 + 1 (uniform).
+        const int i0 = min(xrow(r * kWgThreads + wave * kWave), kMaxRows - 2);
+        const uint16_t *const x0 = rp.x[i0], *const x1 = rp.x[i0 + 1];
+        const int idx = min(r * kWgThreads + tid, xlast);
+        const int i = xrow(idx), c = idx - (int)__umul24((uint32_t)i, (uint32_t)vecs);
+        xv[r] = *reinterpret_cast<const uint4 *>((i == i0 ? x0 : x1) + kbase + 8 * c);
+      }
+    }
+  }
 
   // This workgroup's units [cu_u0, cu_u1) and this wave's piece of them.
   const CuSplit q = cu_split(group, pl);
@@ -908,7 +953,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     std::conditional_t<kAhead, uint16_t, uint32_t> scb;
   };
   Slot S0, S1;
-  int tile = (int)((uint32_t)u0 / (uint32_t)pl.kp);
+  int tile = (int)div_by<7>((uint32_t)u0, pl);
   int b = u0 - tile * pl.kp;
   int pt = tile, pb = b, pu = u0;  // next unit to request
   auto advance = [&](int &t, int &bb) {
@@ -941,43 +986,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   constexpr uint32_t kMaskAddr = TAB == kPairTable ? 0xFFFCu : TAB == kCodeTable ? 0x1FFEu : 0x3FFCu;
   bool ahead = false;  // the first unit's first phase is decoded (its row scales are in range)
   bf16x8 aw[4];        // its weights
-  const int vecs = panel_k / 8;
-  const int xtotal = pl.m * vecs;  // <= kStageRegs * kWgThreads (the x panel fits in LDS)
-  // Staged x vector idx (16 B) is row i = idx / vecs, column idx - i * vecs;
-  // rows are one vector longer in LDS, so it lands at byte 16 (idx + i).
-  // A wave skips the rounds that start past the panel; lanes past it take
-  // the panel's last vector (a second load of it and an identical store).
-  auto xrow = [&](int idx) { return (int)(__umul24((uint32_t)idx >> 5, pl.xmul) >> pl.xshift); };
   {
-    uint4 xv[kStageRegs];
-#pragma unroll
-    for (int r = 0; r < kStageRegs; ++r) xv[r] = uint4{0u, 0u, 0u, 0u};  // defined on every path: keeps xv in registers
-    const int xlast = xtotal - 1;
-    if (pl.x_contiguous) {
-      // Rows K elements apart: vector idx is 16 (idx + i (panels - 1) vecs)
-      // bytes past row 0's part of the panel.
-      const unsigned char *const xb = reinterpret_cast<const unsigned char *>(rp.x[0] + kbase);
-      const uint32_t pstep = (uint32_t)((pl.panels - 1) * vecs);
-#pragma unroll
-      for (int r = 0; r < kStageRegs; ++r) {
-        if (r * kWgThreads + wave * kWave < xtotal) {
-          const int idx = min(r * kWgThreads + tid, xlast);
-          xv[r] = *reinterpret_cast<const uint4 *>(xb + ((uint32_t)idx + __umul24((uint32_t)xrow(idx), pstep)) * 16u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kStageRegs; ++r) {
-        if (r * kWgThreads + wave * kWave >= xtotal) continue;
-        // A wave's 64 vectors start at a multiple of 64 and a row holds a
-        // multiple of 32 of them, so they lie in rows i0 and i0 + 1 (uniform).
-        const int i0 = min(xrow(r * kWgThreads + wave * kWave), kMaxRows - 2);
-        const uint16_t *const x0 = rp.x[i0], *const x1 = rp.x[i0 + 1];
-        const int idx = min(r * kWgThreads + tid, xlast);
-        const int i = xrow(idx), c = idx - (int)__umul24((uint32_t)i, (uint32_t)vecs);
-        xv[r] = *reinterpret_cast<const uint4 *>((i == i0 ? x0 : x1) + kbase + 8 * c);
-      }
-    }
     if (wave == 0) {
       uint64_t v = 0;
 #pragma unroll
@@ -1041,7 +1050,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   // Whether the range holds a tile shared with another workgroup (for one
   // K panel only its first or last tile can be).
   const bool holds_cross =
-      active && (cross(tf) || cross((int)((uint32_t)(u1 > 0 ? u1 - 1 : 0) / (uint32_t)pl.kp)));
+      active && (cross(tf) || cross((int)div_by<7>((uint32_t)(u1 > 0 ? u1 - 1 : 0), pl)));
   // Partials kept for the barrier combine: of the range's first tile (when
   // it ends inside the loop) and of its last tile. With two matrices the
   // first tile's pair waits in this wave's slot of `kept` (global memory)
@@ -1434,14 +1443,16 @@ Plan make_plan(int m, int n, int k, int cus, int table, bool two) {
     // Multipliers of div_by: l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
     auto base_of = [](uint32_t len) -> uint32_t { return len >= kWaves ? len / kWaves : len > 0 ? 1 : 0; };
     const uint32_t bl = base_of((uint32_t)pl.cq + 1), bs = base_of((uint32_t)pl.cq);
-    const uint32_t divisors[6] = {(uint32_t)pl.cq + 1, (uint32_t)pl.cq, bl + 1, bl, bs + 1, bs};
+    const uint32_t divisors[8] = {(uint32_t)pl.cq + 1, (uint32_t)pl.cq, bl + 1, bl, bs + 1, bs,
+                                  (uint32_t)pl.panels, (uint32_t)pl.kp};
     pl.dl = 0;
-    for (int i = 0; i < 6; ++i) {
+    pl.dl2 = 0;
+    for (int i = 0; i < 8; ++i) {
       const uint32_t d = divisors[i];
       uint32_t l = 0;
       while ((1ull << l) < d) ++l;
       pl.dm[i] = d <= 1 ? 0u : (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
-      pl.dl |= (d <= 1 ? 0u : l) << (5 * i);
+      (i < 6 ? pl.dl : pl.dl2) |= (d <= 1 ? 0u : l) << (5 * (i % 6));
     }
   }
   // Pieces sharing one tile (per panel): at most (kp - 1) / (shortest piece) + 2.
