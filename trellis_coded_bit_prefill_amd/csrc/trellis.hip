@@ -850,10 +850,13 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     asm volatile("" : "+v"(l));
     return l;
   };
-  // Row 0's pointer is read with the plan (the empty asm keeps the read at
-  // the top, not in a branch below where it would wait on its own).
+  // Row 0's pointer and this wave's output row pointer (one per wave) are
+  // read with the plan: the empty asm keeps the reads at the top, not further
+  // down where each would wait on its own.
+  static_assert(kMaxRows == kWaves, "one output row pointer per wave");
   const uint16_t *const x_row0 = rp.x[0];
-  asm volatile("" ::"s"(x_row0));
+  const uint64_t out_row = reinterpret_cast<uint64_t>(rp.out[wave]);
+  asm volatile("" ::"s"(x_row0), "s"(out_row));
   const int group = (int)div_by<6>(blockIdx.x, pl);
   const int panel = (int)blockIdx.x - group * pl.panels;
   const int panel_k = pl.kp * 256;
@@ -987,25 +990,27 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
   bool ahead = false;  // the first unit's first phase is decoded (its row scales are in range)
   bf16x8 aw[4];        // its weights
   {
-    if (wave == 0) {
-      uint64_t v = 0;
-#pragma unroll
-      for (int r = 0; r < kMaxRows; ++r)
-        if (lane == r) v = reinterpret_cast<uint64_t>(rp.out[r]);
-      if (lane < kMaxRows) s_rows[lane] = v;
-      // counters of the barrier-free combine start at zero
-      if (pl.slots_off > 0 && lane < kWaves)
-        reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes)[lane] = 0u;
-    }
+    // counters of the barrier-free combine start at zero
+    if (wave == 0 && pl.slots_off > 0 && lane < kWaves)
+      reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes)[lane] = 0u;
     request(S0, std::false_type{});
+    // (every thread builds the same number of entries: no loop control)
+    static_assert(2048 % kWgThreads == 0, "table entries divide among the threads");
     if constexpr (TAB == kPairTable) {
-      for (int e = tid; e < 16384; e += kWgThreads) s_table[e] = pair_entry((uint32_t)e);
+#pragma unroll
+      for (int r = 0; r < 16384 / kWgThreads; ++r) s_table[r * kWgThreads + tid] = pair_entry((uint32_t)(r * kWgThreads + tid));
     } else if constexpr (TAB == kCodeTable) {
-      for (int e = tid; e < 2048; e += kWgThreads) s_table[e] = code_entry_pair((uint32_t)e);
+#pragma unroll
+      for (int r = 0; r < 2048 / kWgThreads; ++r)
+        s_table[r * kWgThreads + tid] = code_entry_pair((uint32_t)(r * kWgThreads + tid));
     } else {
-      for (int e = tid; e < 4096; e += kWgThreads)
-        s_table[e] = __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)e)));
+#pragma unroll
+      for (int r = 0; r < 4096 / kWgThreads; ++r)
+        s_table[r * kWgThreads + tid] =
+            __builtin_bit_cast(uint32_t, trellis_value(code_of((uint32_t)(r * kWgThreads + tid))));
     }
+    // Output row pointers to LDS, one per wave (read at the top).
+    if (lane == 0) s_rows[wave] = out_row;
     if constexpr (kAhead) {
       lds_barrier();  // the table is built
     }
