@@ -197,23 +197,27 @@ __device__ __forceinline__ int piece_start(const CuSplit &q, int p) {
   return q.u0 + p * q.base + (p < q.ce ? p : q.ce) + (tail > 0 ? tail : 0);
 }
 
+// Position of the piece holding unit q.u0 + o (0 <= o < q.len) in the split q
+// of workgroup c: pieces of base + 1 units (the first ce and the last h) and
+// of base units.
+__device__ __forceinline__ int piece_in(const CuSplit &q, int c, int o, const Plan &pl) {
+  const int x1 = q.ce * (q.base + 1), x2 = x1 + (q.s - q.h - q.ce) * q.base;
+  // this workgroup's base + 1 and base (the divisors differ with its length)
+  const bool lng = c < pl.cr;
+  const uint32_t m1 = lng ? pl.dm[2] : pl.dm[4], l1 = (pl.dl >> (lng ? 10 : 20)) & 31u;
+  const uint32_t m0 = lng ? pl.dm[3] : pl.dm[5], l0 = (pl.dl >> (lng ? 15 : 25)) & 31u;
+  if (o < x1) return (int)div_magic((uint32_t)o, m1, l1);
+  if (o < x2) return q.ce + (int)div_magic((uint32_t)(o - x1), m0, l0);
+  return q.s - q.h + (int)div_magic((uint32_t)(o - x2), m1, l1);
+}
+
 // Global index (workgroup * 16 + position) of the piece holding unit u;
 // consecutive pieces in unit order have consecutive indices.
 __device__ __forceinline__ int piece_of(int u, const Plan &pl) {
   const int cut = pl.cr * (pl.cq + 1);
   const int c = u < cut ? (int)div_by<0>((uint32_t)u, pl) : pl.cr + (int)div_by<1>((uint32_t)(u - cut), pl);
   const CuSplit q = cu_split(c, pl);
-  const int o = u - q.u0;
-  const int x1 = q.ce * (q.base + 1), x2 = x1 + (q.s - q.h - q.ce) * q.base;
-  // this workgroup's base + 1 and base (the divisors differ with its length)
-  const bool lng = c < pl.cr;
-  const uint32_t m1 = lng ? pl.dm[2] : pl.dm[4], l1 = (pl.dl >> (lng ? 10 : 20)) & 31u;
-  const uint32_t m0 = lng ? pl.dm[3] : pl.dm[5], l0 = (pl.dl >> (lng ? 15 : 25)) & 31u;
-  int p;
-  if (o < x1) p = (int)div_magic((uint32_t)o, m1, l1);
-  else if (o < x2) p = q.ce + (int)div_magic((uint32_t)(o - x1), m0, l0);
-  else p = q.s - q.h + (int)div_magic((uint32_t)(o - x2), m1, l1);
-  return c * kWaves + p;
+  return c * kWaves + piece_in(q, c, u - q.u0, pl);
 }
 
 // Lane (j, g) of a wave: j = row of the 16-row tile (B column) and x row (A
@@ -1081,9 +1085,9 @@ __global__ __launch_bounds__(kWgThreads) void prefill_kernel(const uint32_t *__r
     uint32_t *cnt = reinterpret_cast<uint32_t *>(xl + pl.slots_off + kSlotBytes);
     slots[((seg * 2 + which) * NH) * kWave + lane] = v;
     if constexpr (TWO) slots[((seg * 2 + which) * NH + 1) * kWave + lane] = v2;
-    const int p0 = piece_of(T * pl.kp, pl);
-    const int lead = p0 - group * kWaves;
-    const int contrib = piece_of(T * pl.kp + pl.kp - 1, pl) - p0 + 1;
+    // (T lies in this workgroup's units: its pieces are found in this split)
+    const int lead = piece_in(q, group, T * pl.kp - cu_u0, pl);
+    const int contrib = piece_in(q, group, T * pl.kp + pl.kp - 1 - cu_u0, pl) - lead + 1;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     uint32_t old = 0;
     if (lane == 0) old = __hip_atomic_fetch_add(&cnt[lead], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
