@@ -1,13 +1,19 @@
 """The exact division that locates a unit's piece in the prefill kernel.
 
-The kernel divides by a handful of per-call divisors (units per workgroup
-and the pieces' lengths) with host-computed multipliers: for d > 1,
+The kernel divides by a handful of per-call divisors (units per workgroup,
+the pieces' lengths, the K panels and the blocks per panel) with
+host-computed multipliers: for d > 1,
 l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, and then
 n / d = (t + ((n - t) >> 1)) >> (l - 1) with t = floor(n m / 2^32)
 (Granlund and Montgomery, "Division by invariant integers using
 multiplication", 1994). This checks the method itself against integer
 division over the divisors the library can meet (1 .. 2^28) and all 32-bit
 dividends at the edges; the GPU parity tests check the kernel's use of it.
+
+Staging x divides a vector index idx < 2^14 by the vectors per row, kp * 32:
+(idx >> 5) / kp with n = idx >> 5 < 2^9 is (n * m) >> (9 + l) for
+l = ceil(log2 kp), m = ceil(2^(9 + l) / kp), one 24-bit multiply (the same
+paper's round-up method for N-bit dividends).
 """
 import random
 
@@ -45,3 +51,19 @@ def test_division_is_exact():
         for n in ns:
             if 0 <= n < 2 ** 32:
                 assert divide(n, m, l) == n // d, (n, d)
+
+
+def row_multiplier(kp):
+    l = (kp - 1).bit_length()  # ceil(log2 kp)
+    return -(-(1 << (9 + l)) // kp), 9 + l
+
+
+def test_staging_row_multiplier_is_exact():
+    # every blocks-per-panel count up to 512 (x fits in LDS up to 312) and
+    # every 9-bit quotient input
+    for kp in range(1, 513):
+        m, s = row_multiplier(kp)
+        assert m < 2 ** 24
+        for n in range(512):
+            assert n * m < 2 ** 32
+            assert (n * m) >> s == n // kp, (n, kp)
